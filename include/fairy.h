@@ -1,0 +1,208 @@
+/*
+ * fairy.h -- libfairy: the multiplication-free 2-bit complex linear layer
+ * (iFairy / Fairy±i, Fairy2i) on AMD MI355X (gfx950).
+ *
+ *   y = sum_k [ Q(U_k) x + Q(W_k) conj(x) ]
+ *
+ * Each weight is a 2-bit PhaseQuant code c in {0,1,2,3} standing for the
+ * codeword i^c in {1, i, -1, -i}; each (matrix, stage) carries two per-axis
+ * scales (s_re, s_im).  Products reduce to sign flips and real/imag swaps
+ * feeding four fp32 accumulators; the scales are applied once at the end.
+ *
+ * Sources (web pages; cited by page title and section):
+ *   [Fairy2i article]  "复数域低比特量化框架Fairy2i" (hotelren.com/news/3072820):
+ *                      §2.1 widely-linear conversion, §3.1 codebook and phase
+ *                      rule, §3.2 axis scales, §4.1 recursive residual,
+ *                      §4.2 multiplication-free matmul, §5.3 "verify split
+ *                      real/imag handling".
+ *   [iFairy talk]      minutes of the talk "iFairy: 2-bit复数基座大模型"
+ *                      (news.43b.com.cn/a/865699.html), §2.3.1: times i is a
+ *                      real/imag swap with a negation.
+ *   [iFairy abstract]  arXiv 2508.05571 record: one non-zero axis per code,
+ *                      inference with additions and swaps only.
+ *   [Fairy2i abstract] chatpaper.ai record of Fairy2i: widely-linear form,
+ *                      recursive residual quantisation, multiplication-free
+ *                      accumulation.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - All data pointers are DEVICE pointers unless stated otherwise.  The
+ *    fairy_clinear descriptor itself is read on the host.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is asynchronous on that stream; the caller keeps every buffer alive
+ *    until the stream has synchronised.
+ *  - The caller allocates and owns every buffer.  The library allocates no
+ *    device memory, keeps no pointer after a call returns and has no mutable
+ *    global state; calls on different streams may overlap.
+ *  - Arguments are validated on the host before any launch.  A call that
+ *    returns an error launches nothing and writes nothing.  Calls never
+ *    throw, abort or print.
+ *  - Complex data is always split into separate real and imaginary planes
+ *    (structure of arrays), as [Fairy2i article §5.3] asks.
+ *  - Inputs must be finite.  NaN/Inf inputs are undefined behaviour (not
+ *    checked).
+ */
+#ifndef FAIRY_H
+#define FAIRY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FAIRY_ABI_VERSION 1
+
+typedef enum {
+    FAIRY_OK = 0,
+    FAIRY_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad enum, misalignment */
+    FAIRY_ERR_UNSUPPORTED = 2,  /* valid request outside what v1 implements */
+    FAIRY_ERR_HIP = 3,          /* a HIP runtime call or launch failed */
+    FAIRY_ERR_WORKSPACE = 4     /* workspace missing or too small */
+} fairy_status;
+
+/* Packed code layouts.  Both hold 16 two-bit codes per uint32.
+ *  ROW16   : words [planes][rows][m/16]; column 16w+t of a row sits at
+ *            bits 2t..2t+1 of its word w.  Canonical interchange layout.
+ *  TILED64 : words [rows][ceil(m/64)][planes][4]; the 64 columns of group g
+ *            of every plane of a row are contiguous (planes interleaved), and
+ *            word u of the group holds column 64g+16u+t at bit offset
+ *            (t even ? 14-t : 31-t).  Columns >= m hold code 0.  This is the
+ *            layout the GEMV/GEMM kernels read: one 128-bit load per lane per
+ *            plane, and after a left shift by 2k the codes of columns 2k and
+ *            2k+1 sit in the sign and top exponent bits of a bf16 pair.
+ * Inside a word, a code's bit 1 is the sign of its codeword and bit 0 its
+ * axis (0 = real, 1 = imaginary): code c <-> i^c. */
+typedef enum {
+    FAIRY_LAYOUT_ROW16 = 0,
+    FAIRY_LAYOUT_TILED64 = 1
+} fairy_layout;
+
+/* Activation element types (SoA planes, row-major [batch][ldx]). */
+typedef enum {
+    FAIRY_F32 = 0,
+    FAIRY_BF16 = 1,  /* raw bfloat16 bit patterns */
+    FAIRY_I8 = 2     /* plain integers, scale 1 */
+} fairy_dtype;
+
+/* Prefill GEMM algorithm. */
+typedef enum {
+    FAIRY_ALGO_AUTO = 0,
+    FAIRY_ALGO_VALU = 1,  /* direct decode on the vector ALUs */
+    FAIRY_ALGO_MFMA = 2   /* codes expanded to ternary planes, matrix cores */
+} fairy_algo;
+
+/* A quantised complex linear layer.
+ *  n, m      : complex output and input sizes (rows x columns).
+ *  stages    : S, number of recursive residual stages (1..8).
+ *  has_conj  : 1 for the widely-linear form U x + W conj(x), 0 for U x only.
+ *  Planes    : P = S * (1 + has_conj), ordered U_1..U_S, W_1..W_S.
+ *  layout    : FAIRY_LAYOUT_TILED64 for fairy_cgemv / fairy_cgemm.
+ *  packed    : device, fairy_packed_words(n, m, P, layout) uint32 words,
+ *              16-byte aligned.
+ *  scales    : device float [P][2] = {s_re, s_im} per plane. */
+typedef struct {
+    int64_t n, m;
+    int32_t stages, has_conj;
+    int32_t layout;
+    const uint32_t* packed;
+    const float* scales;
+} fairy_clinear;
+
+int32_t fairy_abi_version(void);
+
+/* Static, human-readable name of a status code; never NULL. */
+const char* fairy_status_string(fairy_status status);
+
+/* Widely-linear conversion of a real layer [Fairy2i article §2.1]:
+ * R (row-major [2n][2m] fp32) is split into blocks R11 = R[:n,:m],
+ * R12 = R[:n,m:], R21 = R[n:,:m], R22 = R[n:,m:] and
+ *   ReU = (R11+R22)/2, ImU = (R21-R12)/2, ReW = (R11-R22)/2, ImW = (R12+R21)/2,
+ * each rounded once to fp32 (nearest even).  Then R x equals U x_c + W conj(x_c)
+ * under x_c = x[:m] + i x[m:], y_c = y[:n] + i y[n:].
+ * Outputs u_re, u_im, w_re, w_im are [n][m].  n, m >= 1. */
+fairy_status fairy_real_to_complex(const float* R, int64_t n, int64_t m,
+                                   float* u_re, float* u_im, float* w_re, float* w_im,
+                                   void* stream);
+
+/* Workspace for fairy_phasequant: (stages) x 512 uint64 exponent buckets
+ * plus counts.  Returns 0 for invalid arguments. */
+size_t fairy_phasequant_workspace_bytes(int64_t count, int32_t stages);
+
+/* PhaseQuant with S recursive residual stages [Fairy2i article §3.1, §3.2,
+ * §4.1; iFairy abstract].
+ *   Stage k (k = 1..S) quantises R_k (R_1 = W):
+ *     code  = quadrant of arg(R_k): floor(2 theta/pi + 1/2) mod 4, evaluated by
+ *             exact comparisons; |Re| == |Im| goes to the counter-clockwise
+ *             neighbour; 0 (any signed zeros) -> code 0;
+ *     s_re  = mean |Re R_k| over entries coded +-1, s_im = mean |Im R_k| over
+ *             entries coded +-i: the exact mean rounded once to fp32 (nearest
+ *             even); an empty set gives 0.  Reduction is in exact integers,
+ *             so the result does not depend on launch shape or order;
+ *     R_{k+1} = R_k - (s_re Re(i^c) + i s_im Im(i^c)): one fp32 subtraction
+ *             on the code's axis.
+ *   w_re, w_im : [count] fp32 (a matrix is passed flattened, row-major).
+ *   codes      : [stages][count] uint8 (0..3).
+ *   scales     : [stages][2] fp32 {s_re, s_im}, written on the device.
+ *   resid_re/im: nullable, R_{S+1}.
+ *   workspace  : device, >= fairy_phasequant_workspace_bytes(count, stages),
+ *                8-byte aligned; contents on entry are ignored.
+ * 1 <= count < 2^32, 1 <= stages <= 8. */
+fairy_status fairy_phasequant(const float* w_re, const float* w_im, int64_t count, int32_t stages,
+                              uint8_t* codes, float* scales, float* resid_re, float* resid_im,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of uint32 words of a packed buffer; -1 for invalid arguments. */
+int64_t fairy_packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout);
+
+/* Pack codes [planes][rows][m] (uint8, values 0..3; higher bits ignored)
+ * into `layout`, 16 codes per uint32.  m % 16 == 0 (else UNSUPPORTED);
+ * codes and packed 16-byte aligned. */
+fairy_status fairy_pack(const uint8_t* codes, int32_t planes, int64_t rows, int64_t m,
+                        int32_t layout, uint32_t* packed, void* stream);
+
+/* Inverse of fairy_pack (padding columns are not written). */
+fairy_status fairy_unpack(const uint32_t* packed, int32_t planes, int64_t rows, int64_t m,
+                          int32_t layout, uint8_t* codes, void* stream);
+
+/* Workspace bytes fairy_cgemv needs for this layer and batch (0 in v1). */
+size_t fairy_cgemv_workspace_bytes(const fairy_clinear* L, int32_t batch, int32_t xdtype);
+
+/* Decode-time complex GEMV [Fairy2i article §4.2, §2.1; iFairy talk §2.3.1]:
+ *   y[b] = sum_{k<S} What(U_k) x[b] + has_conj * sum_{k<S} What(W_k) conj(x[b]),
+ *   What(c) = s_re Re(i^c) + i s_im Im(i^c),
+ * computed as four accumulators per plane and batch column,
+ *   A1 = sum ReB x_re, A2 = sum ImB x_im, A3 = sum ReB x_im, A4 = sum ImB x_re,
+ * and the epilogue  U plane: y_re += s_re A1 - s_im A2, y_im += s_re A3 + s_im A4;
+ *                   W plane: y_re += s_re A1 + s_im A2, y_im += s_im A4 - s_re A3.
+ *   x_re, x_im : [batch][ldx] of xdtype (F32, BF16 or I8), 16-byte aligned,
+ *                ldx >= m and ldx a multiple of 16 elements.
+ *   y_re, y_im : [batch][ldy] fp32, ldy >= n.  Overwritten.
+ *   acc        : nullable; I8 only: int32 [P][4][batch][n], the exact integer
+ *                accumulators A1..A4 per plane (planes U_1..U_S, W_1..W_S).
+ *   batch      : 1..64.
+ *   workspace  : may be NULL when fairy_cgemv_workspace_bytes() is 0.
+ * float outputs are within 1e-5 relative L2 of the exact result on the same
+ * inputs; integer accumulators are exact. */
+fairy_status fairy_cgemv(const fairy_clinear* L, const void* x_re, const void* x_im,
+                         int32_t xdtype, int32_t batch, int64_t ldx,
+                         float* y_re, float* y_im, int64_t ldy, int32_t* acc,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fairy_cgemm needs. */
+size_t fairy_cgemm_workspace_bytes(const fairy_clinear* L, int64_t M, int32_t xdtype, int32_t algo);
+
+/* Prefill GEMM: fairy_cgemv over M >= 1 token rows (same semantics, same
+ * argument rules with batch replaced by M; acc is [P][4][M][n] for I8).
+ * algo: AUTO, VALU (any dtype) or MFMA (BF16 or I8; codes expanded to
+ * ternary {-1,0,1} planes feeding the matrix cores). */
+fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x_im,
+                         int32_t xdtype, int64_t M, int64_t ldx,
+                         float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FAIRY_H */
