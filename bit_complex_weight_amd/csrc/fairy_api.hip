@@ -1,0 +1,210 @@
+// fairy_api.hip -- the C ABI of libfairy (include/fairy.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime; an invalid call launches nothing and writes nothing.  Errors
+// are reported as fairy_status codes, never by exceptions or printing.
+#include "fairy_internal.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+fairy_status from_hip(hipError_t e) { return e == hipSuccess ? FAIRY_OK : FAIRY_ERR_HIP; }
+
+// Launch errors are read with hipGetLastError() after each launch.  Another
+// component on this thread (for example an event query that returned
+// hipErrorNotReady) may have left a stale error behind; drop it once the
+// arguments have been validated and just before the first launch.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool valid_layout(int32_t l) { return l == FAIRY_LAYOUT_ROW16 || l == FAIRY_LAYOUT_TILED64; }
+
+bool valid_dtype(int32_t d) { return d == FAIRY_F32 || d == FAIRY_BF16 || d == FAIRY_I8; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+// Largest m the v1 kernels stage in LDS (one batch column, 64 KiB).
+int64_t max_m_for(int32_t xdtype)
+{
+    return xdtype == FAIRY_F32 ? 8192 : xdtype == FAIRY_BF16 ? 16384 : 32768;
+}
+
+// Checks shared by fairy_cgemv and fairy_cgemm.  Returns FAIRY_OK and fills
+// the launcher's view of the layer on success.
+fairy_status check_layer_call(const fairy_clinear* L, const void* x_re, const void* x_im, int32_t xdtype,
+                              int64_t rows, int64_t ldx, const float* y_re, const float* y_im, int64_t ldy,
+                              const int32_t* acc, fairy::LayerArgs* out)
+{
+    if (!L || !x_re || !x_im || !y_re || !y_im) return FAIRY_ERR_INVALID_ARG;
+    if (L->n < 1 || L->m < 1 || L->n > kMaxDim || L->m > kMaxDim) return FAIRY_ERR_INVALID_ARG;
+    if (L->stages < 1 || L->stages > 8) return FAIRY_ERR_INVALID_ARG;
+    if (L->has_conj != 0 && L->has_conj != 1) return FAIRY_ERR_INVALID_ARG;
+    if (!valid_layout(L->layout)) return FAIRY_ERR_INVALID_ARG;
+    if (!L->packed || !L->scales) return FAIRY_ERR_INVALID_ARG;
+    if (!valid_dtype(xdtype)) return FAIRY_ERR_INVALID_ARG;
+    if (rows < 1) return FAIRY_ERR_INVALID_ARG;
+    if (ldx < L->m || ldy < L->n) return FAIRY_ERR_INVALID_ARG;
+    if (acc && xdtype != FAIRY_I8) return FAIRY_ERR_INVALID_ARG;
+    if (!aligned(L->packed, 16) || !aligned(x_re, 16) || !aligned(x_im, 16) || !aligned(L->scales, 4) ||
+        !aligned(y_re, 4) || !aligned(y_im, 4) || (acc && !aligned(acc, 4)))
+        return FAIRY_ERR_INVALID_ARG;
+    if (ldx % 16 != 0) return FAIRY_ERR_INVALID_ARG;
+    if (L->layout != FAIRY_LAYOUT_TILED64) return FAIRY_ERR_UNSUPPORTED;
+    if (L->m % 16 != 0) return FAIRY_ERR_UNSUPPORTED;
+    if (L->m > max_m_for(xdtype)) return FAIRY_ERR_UNSUPPORTED;
+    out->packed = L->packed;
+    out->scales = L->scales;
+    out->n = L->n;
+    out->m = L->m;
+    out->stages = L->stages;
+    out->planes = L->stages * (1 + L->has_conj);
+    return FAIRY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fairy_abi_version(void) { return FAIRY_ABI_VERSION; }
+
+const char* fairy_status_string(fairy_status status)
+{
+    switch (status) {
+    case FAIRY_OK: return "FAIRY_OK";
+    case FAIRY_ERR_INVALID_ARG: return "FAIRY_ERR_INVALID_ARG: null pointer, bad size, bad enum or misalignment";
+    case FAIRY_ERR_UNSUPPORTED: return "FAIRY_ERR_UNSUPPORTED: valid request outside what this version implements";
+    case FAIRY_ERR_HIP: return "FAIRY_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case FAIRY_ERR_WORKSPACE: return "FAIRY_ERR_WORKSPACE: workspace missing or too small";
+    }
+    return "FAIRY_ERR_UNKNOWN: not a fairy_status value";
+}
+
+fairy_status fairy_real_to_complex(const float* R, int64_t n, int64_t m, float* u_re, float* u_im,
+                                   float* w_re, float* w_im, void* stream)
+{
+    if (!R || !u_re || !u_im || !w_re || !w_im) return FAIRY_ERR_INVALID_ARG;
+    if (n < 1 || m < 1 || n > kMaxDim || m > kMaxDim) return FAIRY_ERR_INVALID_ARG;
+    if (!aligned(R, 4) || !aligned(u_re, 4) || !aligned(u_im, 4) || !aligned(w_re, 4) || !aligned(w_im, 4))
+        return FAIRY_ERR_INVALID_ARG;
+    clear_stale_error();
+    return from_hip(fairy::launch_real_to_complex(R, n, m, u_re, u_im, w_re, w_im, as_stream(stream)));
+}
+
+size_t fairy_phasequant_workspace_bytes(int64_t count, int32_t stages)
+{
+    if (count < 1 || count >= ((int64_t)1 << 32) || stages < 1 || stages > 8) return 0;
+    return fairy::phasequant_workspace_bytes(stages);
+}
+
+fairy_status fairy_phasequant(const float* w_re, const float* w_im, int64_t count, int32_t stages,
+                              uint8_t* codes, float* scales, float* resid_re, float* resid_im, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    if (!w_re || !w_im || !codes || !scales) return FAIRY_ERR_INVALID_ARG;
+    if (count < 1 || count >= ((int64_t)1 << 32)) return FAIRY_ERR_INVALID_ARG;
+    if (stages < 1 || stages > 8) return FAIRY_ERR_INVALID_ARG;
+    if (!aligned(w_re, 4) || !aligned(w_im, 4) || !aligned(scales, 4) || (resid_re && !aligned(resid_re, 4)) ||
+        (resid_im && !aligned(resid_im, 4)))
+        return FAIRY_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < fairy::phasequant_workspace_bytes(stages) || !aligned(workspace, 8))
+        return FAIRY_ERR_WORKSPACE;
+    clear_stale_error();
+    return from_hip(fairy::launch_phasequant(w_re, w_im, count, stages, codes, scales, resid_re, resid_im,
+                                             workspace, as_stream(stream)));
+}
+
+int64_t fairy_packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout)
+{
+    if (rows < 1 || m < 1 || planes < 1 || planes > 16 || !valid_layout(layout)) return -1;
+    if (rows > kMaxDim || m > kMaxDim) return -1;
+    if (layout == FAIRY_LAYOUT_ROW16 && m % 16 != 0) return -1;
+    return fairy::packed_words(rows, m, planes, layout);
+}
+
+static fairy_status check_pack(const void* codes, int32_t planes, int64_t rows, int64_t m, int32_t layout,
+                               const void* packed)
+{
+    if (!codes || !packed) return FAIRY_ERR_INVALID_ARG;
+    if (planes < 1 || planes > 16 || rows < 1 || m < 1 || rows > kMaxDim || m > kMaxDim)
+        return FAIRY_ERR_INVALID_ARG;
+    if (!valid_layout(layout)) return FAIRY_ERR_INVALID_ARG;
+    if (!aligned(codes, 16) || !aligned(packed, 16)) return FAIRY_ERR_INVALID_ARG;
+    if (m % 16 != 0) return FAIRY_ERR_UNSUPPORTED;
+    return FAIRY_OK;
+}
+
+fairy_status fairy_pack(const uint8_t* codes, int32_t planes, int64_t rows, int64_t m, int32_t layout,
+                        uint32_t* packed, void* stream)
+{
+    fairy_status st = check_pack(codes, planes, rows, m, layout, packed);
+    if (st != FAIRY_OK) return st;
+    clear_stale_error();
+    return from_hip(fairy::launch_pack(codes, planes, rows, m, layout, packed, as_stream(stream)));
+}
+
+fairy_status fairy_unpack(const uint32_t* packed, int32_t planes, int64_t rows, int64_t m, int32_t layout,
+                          uint8_t* codes, void* stream)
+{
+    fairy_status st = check_pack(codes, planes, rows, m, layout, packed);
+    if (st != FAIRY_OK) return st;
+    clear_stale_error();
+    return from_hip(fairy::launch_unpack(packed, planes, rows, m, layout, codes, as_stream(stream)));
+}
+
+size_t fairy_cgemv_workspace_bytes(const fairy_clinear* L, int32_t batch, int32_t xdtype)
+{
+    (void)L;
+    (void)batch;
+    (void)xdtype;
+    return 0;
+}
+
+fairy_status fairy_cgemv(const fairy_clinear* L, const void* x_re, const void* x_im, int32_t xdtype,
+                         int32_t batch, int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (batch < 1 || batch > 64) return FAIRY_ERR_INVALID_ARG;
+    fairy::LayerArgs la;
+    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, acc, &la);
+    if (st != FAIRY_OK) return st;
+    clear_stale_error();
+    return from_hip(fairy::launch_cgemv(la, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, acc, as_stream(stream)));
+}
+
+size_t fairy_cgemm_workspace_bytes(const fairy_clinear* L, int64_t M, int32_t xdtype, int32_t algo)
+{
+    fairy::LayerArgs la;
+    if (!L || M < 1) return 0;
+    la.packed = L->packed;
+    la.scales = L->scales;
+    la.n = L->n;
+    la.m = L->m;
+    la.stages = L->stages;
+    la.planes = L->stages * (1 + (L->has_conj ? 1 : 0));
+    return fairy::cgemm_workspace_bytes(la, M, xdtype, algo);
+}
+
+fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x_im, int32_t xdtype, int64_t M,
+                         int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (M < 1 || M > kMaxDim) return FAIRY_ERR_INVALID_ARG;
+    if (algo != FAIRY_ALGO_AUTO && algo != FAIRY_ALGO_VALU && algo != FAIRY_ALGO_MFMA) return FAIRY_ERR_INVALID_ARG;
+    fairy::LayerArgs la;
+    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, &la);
+    if (st != FAIRY_OK) return st;
+    if (algo == FAIRY_ALGO_MFMA && xdtype == FAIRY_F32) return FAIRY_ERR_UNSUPPORTED;
+    const size_t need = fairy::cgemm_workspace_bytes(la, M, xdtype, algo);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FAIRY_ERR_WORKSPACE;
+    clear_stale_error();
+    hipError_t e = fairy::launch_cgemm(la, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, algo, workspace,
+                                       as_stream(stream));
+    if (e == hipErrorNotSupported) return FAIRY_ERR_UNSUPPORTED;
+    return from_hip(e);
+}
+
+}  // extern "C"

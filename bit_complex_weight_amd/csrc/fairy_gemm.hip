@@ -1,0 +1,29 @@
+// fairy_gemm.hip -- prefill complex GEMM on gfx950.
+//
+// The prefill layer is the decode layer applied to M token rows at once
+// [Fairy2i article §4.2]; at M in the thousands it is a dense contraction.
+#include "fairy_internal.h"
+
+namespace fairy {
+
+size_t cgemm_workspace_bytes(const LayerArgs& L, int64_t M, int32_t xdtype, int32_t algo)
+{
+    (void)L;
+    (void)M;
+    (void)xdtype;
+    (void)algo;
+    return 0;
+}
+
+hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype, int64_t M,
+                        int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,
+                        void* workspace, hipStream_t s)
+{
+    (void)workspace;
+    if (algo == FAIRY_ALGO_MFMA) return hipErrorNotSupported;
+    // VALU path: the decode kernel streams the token rows through LDS in
+    // chunks, re-reading the (L2-resident) codes per chunk.
+    return launch_cgemv(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, s);
+}
+
+}  // namespace fairy

@@ -1,0 +1,122 @@
+// fairy_internal.h -- shared declarations of the HIP library (not installed).
+//
+// Device helpers common to the kernels: the 2-bit code decode and the
+// cross-lane (DPP / ds_swizzle) reductions.  Host launchers are declared at
+// the bottom; fairy_api.hip validates arguments and calls them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fairy.h"
+
+namespace fairy {
+
+// ---------------------------------------------------------------------------
+// Code decode
+// ---------------------------------------------------------------------------
+// A code c = 2*s + a holds the sign s of its codeword i^c and its axis a
+// (0 = real, 1 = imaginary).  [Fairy2i article §3.1; iFairy abstract: every
+// codeword has exactly one non-zero axis.]
+//
+// TILED64 words store column t of a 16-column word at bit (t even ? 14-t : 31-t),
+// so after `w << 2k` the codes of columns 2k (low half) and 2k+1 (high half)
+// occupy bits 15:14 and 31:30.  Read as a bfloat16 pair, masking with
+// 0xC000C000 leaves the sign bit and the top exponent bit: the value is
+// +-2 when that exponent bit is set and +-0 otherwise.  Hence
+//   ImB pair (x2) = ws & 0xC000C000                  (axis bit set  -> +-2)
+//   ReB pair (x2) = (ws ^ 0x40004000) & 0xC000C000   (axis bit clear -> +-2)
+// Two bit operations per two codes and no multiplies; the factor 2 is
+// removed once in the epilogue.
+__device__ __forceinline__ void decode_bf16_pair(uint32_t w, int k, uint32_t& re2, uint32_t& im2)
+{
+    const uint32_t ws = w << (2 * k);
+    im2 = ws & 0xC000C000u;
+    re2 = (ws ^ 0x40004000u) & 0xC000C000u;
+}
+
+// Column t of a TILED64 word -> the shift that moves its code to bits 31:30,
+// where, read as fp32, the same masks give +-2 / +-0.
+__device__ __forceinline__ int f32_shift(int t) { return (t & 1) ? (t - 1) : (16 + t); }
+
+// int8 ternary planes for dot4: the four columns whose codes share bit offset
+// 2s inside each byte of a word are, by byte b = 0..3,
+//   t = 14-2s, 6-2s, 15-2s, 7-2s.
+// v_perm turns four 2-bit selectors into four {-1,0,1} bytes.
+__device__ __forceinline__ int i8_group_col(int s, int b)
+{
+    return (b == 0) ? 14 - 2 * s : (b == 1) ? 6 - 2 * s : (b == 2) ? 15 - 2 * s : 7 - 2 * s;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums over aligned groups of W lanes (W = 2..64), result in every
+// lane of the group.  Butterflies: DPP quad_perm for distances 1 and 2,
+// ds_swizzle (bit mode, xor) for 4, 8, 16 and a bpermute for 32.  Every lane
+// adds the same pair of operands at every step, so all lanes of a group hold
+// bit-identical results.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int swz_xor4(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x101F); }
+__device__ __forceinline__ int swz_xor8(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x201F); }
+__device__ __forceinline__ int swz_xor16(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += __int_as_float(dpp_xor1(__float_as_int(v)));
+    if (W >= 4) v += __int_as_float(dpp_xor2(__float_as_int(v)));
+    if (W >= 8) v += __int_as_float(swz_xor4(__float_as_int(v)));
+    if (W >= 16) v += __int_as_float(swz_xor8(__float_as_int(v)));
+    if (W >= 32) v += __int_as_float(swz_xor16(__float_as_int(v)));
+    if (W >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ int group_sum_i(int v)
+{
+    v += dpp_xor1(v);
+    if (W >= 4) v += dpp_xor2(v);
+    if (W >= 8) v += swz_xor4(v);
+    if (W >= 16) v += swz_xor8(v);
+    if (W >= 32) v += swz_xor16(v);
+    if (W >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers (arguments already validated)
+// ---------------------------------------------------------------------------
+hipError_t launch_real_to_complex(const float* R, int64_t n, int64_t m, float* u_re, float* u_im,
+                                  float* w_re, float* w_im, hipStream_t s);
+
+size_t phasequant_workspace_bytes(int32_t stages);
+hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count, int32_t stages,
+                             uint8_t* codes, float* scales, float* resid_re, float* resid_im,
+                             void* workspace, hipStream_t s);
+
+int64_t packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout);
+hipError_t launch_pack(const uint8_t* codes, int32_t planes, int64_t rows, int64_t m, int32_t layout,
+                       uint32_t* packed, hipStream_t s);
+hipError_t launch_unpack(const uint32_t* packed, int32_t planes, int64_t rows, int64_t m,
+                         int32_t layout, uint8_t* codes, hipStream_t s);
+
+struct LayerArgs {
+    const uint32_t* packed;
+    const float* scales;
+    int64_t n, m;
+    int32_t stages, planes;
+};
+
+hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype,
+                        int64_t batch, int64_t ldx, float* y_re, float* y_im, int64_t ldy,
+                        int32_t* acc, hipStream_t s);
+
+size_t cgemm_workspace_bytes(const LayerArgs& L, int64_t M, int32_t xdtype, int32_t algo);
+hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype,
+                        int64_t M, int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc,
+                        int32_t algo, void* workspace, hipStream_t s);
+
+}  // namespace fairy

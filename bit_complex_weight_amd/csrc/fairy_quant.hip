@@ -1,0 +1,437 @@
+// fairy_quant.hip -- offline steps of the layer on gfx950:
+//   widely-linear conversion   [Fairy2i article §2.1]
+//   PhaseQuant codes, exact per-axis scales, recursive residual stages
+//                              [Fairy2i article §3.1, §3.2, §4.1]
+//   packing 16 codes per uint32
+// All kernels are streaming (HBM-bound); they are launched on the caller's
+// stream and allocate nothing.
+#include "fairy_internal.h"
+
+namespace fairy {
+namespace {
+
+constexpr int kThreads = 256;
+
+int grid_for(int64_t work, int per_block, int cap)
+{
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+// ---------------------------------------------------------------------------
+// Widely-linear conversion.  Each output is (a +- b)/2 of two fp32 inputs,
+// formed exactly in fp64 and rounded once to fp32 (fp64 sum then fp32 rounding
+// equals direct fp32 rounding because 53 >= 2*24+2; halving is exact).
+// One thread converts four consecutive columns of one row.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float half_sum(float a, float b) { return (float)(((double)a + (double)b) * 0.5); }
+__device__ __forceinline__ float half_diff(float a, float b) { return (float)(((double)a - (double)b) * 0.5); }
+
+__global__ __launch_bounds__(kThreads) void k_real_to_complex4(const float4* __restrict__ R, int64_t n,
+                                                               int64_t m4, float4* __restrict__ ure,
+                                                               float4* __restrict__ uim,
+                                                               float4* __restrict__ wre,
+                                                               float4* __restrict__ wim)
+{
+    const int64_t ld = 2 * m4;
+    for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+        for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < m4;
+             j += (int64_t)gridDim.x * blockDim.x) {
+            const float4 r11 = R[i * ld + j];
+            const float4 r12 = R[i * ld + m4 + j];
+            const float4 r21 = R[(n + i) * ld + j];
+            const float4 r22 = R[(n + i) * ld + m4 + j];
+            const int64_t o = i * m4 + j;
+            ure[o] = make_float4(half_sum(r11.x, r22.x), half_sum(r11.y, r22.y), half_sum(r11.z, r22.z),
+                                 half_sum(r11.w, r22.w));
+            uim[o] = make_float4(half_diff(r21.x, r12.x), half_diff(r21.y, r12.y),
+                                 half_diff(r21.z, r12.z), half_diff(r21.w, r12.w));
+            wre[o] = make_float4(half_diff(r11.x, r22.x), half_diff(r11.y, r22.y),
+                                 half_diff(r11.z, r22.z), half_diff(r11.w, r22.w));
+            wim[o] = make_float4(half_sum(r12.x, r21.x), half_sum(r12.y, r21.y), half_sum(r12.z, r21.z),
+                                 half_sum(r12.w, r21.w));
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_real_to_complex1(const float* __restrict__ R, int64_t n,
+                                                               int64_t m, float* __restrict__ ure,
+                                                               float* __restrict__ uim,
+                                                               float* __restrict__ wre,
+                                                               float* __restrict__ wim)
+{
+    const int64_t ld = 2 * m;
+    for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+        for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < m;
+             j += (int64_t)gridDim.x * blockDim.x) {
+            const float r11 = R[i * ld + j], r12 = R[i * ld + m + j];
+            const float r21 = R[(n + i) * ld + j], r22 = R[(n + i) * ld + m + j];
+            const int64_t o = i * m + j;
+            ure[o] = half_sum(r11, r22);
+            uim[o] = half_diff(r21, r12);
+            wre[o] = half_diff(r11, r22);
+            wim[o] = half_sum(r12, r21);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// PhaseQuant
+// ---------------------------------------------------------------------------
+// Quadrant of arg(a + ib) by exact comparisons: floor(2 theta/pi + 1/2) mod 4;
+// on |a| == |b| the floor sends theta = 45, 135, -135, -45 degrees to
+// codes 1, 2, 3, 0; zero (either sign) -> 0.
+__device__ __forceinline__ uint32_t phase_code(float a, float b)
+{
+    const float A = fabsf(a), B = fabsf(b);
+    if (A > B) return a > 0.0f ? 0u : 2u;
+    if (B > A) return b > 0.0f ? 1u : 3u;
+    if (A == 0.0f) return 0u;
+    return a > 0.0f ? (b > 0.0f ? 1u : 0u) : (b > 0.0f ? 2u : 3u);
+}
+
+// R <- R - (s_re Re(i^c) + i s_im Im(i^c)), one fp32 operation on the code's axis.
+__device__ __forceinline__ void residual_step(float& a, float& b, uint32_t c, float s_re, float s_im)
+{
+    if (c == 0u) a = a - s_re;
+    else if (c == 2u) a = a + s_re;
+    else if (c == 1u) b = b - s_im;
+    else b = b + s_im;
+}
+
+// Workspace per stage: 2 axes x 256 exponent buckets (uint64) + 2 counts.
+// Bucket eb of an axis holds the sum of the 24-bit integer significands of
+// the magnitudes whose biased exponent is eb (subnormals in bucket 1), so the
+// axis sum is exactly  sum_eb bucket[eb] * 2^(eb-150).  Integer sums are
+// order-independent: scales do not depend on launch shape or scheduling.
+constexpr int kBuckets = 512;
+constexpr int kStageWords = kBuckets + 2;
+
+__global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t count)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0ull;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+    v += (uint32_t)__shfl_xor((int)v, 1);
+    v += (uint32_t)__shfl_xor((int)v, 2);
+    v += (uint32_t)__shfl_xor((int)v, 4);
+    v += (uint32_t)__shfl_xor((int)v, 8);
+    v += (uint32_t)__shfl_xor((int)v, 16);
+    v += (uint32_t)__shfl_xor((int)v, 32);
+    return v;
+}
+
+// Stage k: recompute R_k from W with the scales of stages < k (already on
+// the device), write code_k, and add |R_k| on the code's axis into the
+// stage's exponent buckets.
+__global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__ w_re,
+                                                       const float* __restrict__ w_im, int64_t count,
+                                                       int32_t k, const float* __restrict__ scales,
+                                                       uint8_t* __restrict__ codes,
+                                                       unsigned long long* __restrict__ ws)
+{
+    __shared__ unsigned long long s_buck[kBuckets];
+    __shared__ unsigned long long s_cnt[2];
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) s_buck[t] = 0ull;
+    if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0ull;
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < count; base += stride) {
+        const int64_t i = base + threadIdx.x;
+        const bool valid = i < count;
+        int key = 0;
+        uint32_t sig = 0;
+        if (valid) {
+            float a = w_re[i], b = w_im[i];
+            for (int j = 0; j < k; ++j) residual_step(a, b, phase_code(a, b), scales[2 * j], scales[2 * j + 1]);
+            const uint32_t c = phase_code(a, b);
+            codes[(int64_t)k * count + i] = (uint8_t)c;
+            const uint32_t axis = c & 1u;
+            const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
+            const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
+            sig = ex ? (man | 0x800000u) : man;
+            key = (int)(axis * 256u + (ex ? ex : 1u));
+        }
+        // aggregate equal keys across the wave, one LDS atomic per key
+        unsigned long long pending = __ballot(valid);
+        while (pending) {
+            const int leader = __ffsll((long long)pending) - 1;
+            const int k0 = __shfl(key, leader);
+            const bool mine = valid && key == k0;
+            const unsigned long long same = __ballot(mine);
+            const uint32_t tot = wave_sum_u32(mine ? sig : 0u);
+            if (lane == leader) {
+                atomicAdd(&s_buck[k0], (unsigned long long)tot);
+                atomicAdd(&s_cnt[k0 >> 8], (unsigned long long)__popcll(same));
+            }
+            pending &= ~same;
+        }
+    }
+    __syncthreads();
+    unsigned long long* g = ws + (int64_t)k * kStageWords;
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x)
+        if (s_buck[t]) atomicAdd(&g[t], s_buck[t]);
+    if (threadIdx.x < 2 && s_cnt[threadIdx.x]) atomicAdd(&g[kBuckets + threadIdx.x], s_cnt[threadIdx.x]);
+}
+
+// Exact mean -> fp32, nearest even.  N = sum_eb bucket[eb] * 2^(eb-1) is the
+// sum in units of 2^-149; the mean is N / cnt * 2^-149.  Long division yields
+// a quotient with >= 25 significant bits; the bits below the fp32 significand
+// plus the remainder give the round and sticky information.
+constexpr int kLimbs = 13;  // 416 bits: N < 2^(254 + 54)
+
+__device__ float exact_mean_f32(const unsigned long long* __restrict__ buck, unsigned long long cnt)
+{
+    if (cnt == 0ull) return 0.0f;
+    uint32_t N[kLimbs];
+    for (int i = 0; i < kLimbs; ++i) N[i] = 0u;
+    for (int eb = 1; eb < 256; ++eb) {
+        const unsigned long long v = buck[eb];
+        if (!v) continue;
+        const int pos = eb - 1, wi = pos >> 5, sh = pos & 31;
+        uint32_t part[3];
+        part[0] = (uint32_t)(v << sh);
+        part[1] = (uint32_t)(sh ? (v >> (32 - sh)) : (v >> 32));
+        part[2] = (uint32_t)(sh ? (v >> (64 - sh)) : 0ull);
+        unsigned long long carry = 0ull;
+        for (int q = wi; q < kLimbs; ++q) {
+            const unsigned long long add = (q - wi < 3) ? part[q - wi] : 0u;
+            const unsigned long long s = (unsigned long long)N[q] + add + carry;
+            N[q] = (uint32_t)s;
+            carry = s >> 32;
+        }
+    }
+    int T = 0;  // bit length of N
+    for (int q = kLimbs - 1; q >= 0; --q)
+        if (N[q]) { T = 32 * q + (32 - __clz(N[q])); break; }
+    if (T == 0) return 0.0f;
+    const int Lc = 64 - __clzll(cnt);
+    int F = 27 + Lc - T;
+    if (F < 0) F = 0;
+    // N <<= F
+    if (F > 0) {
+        const int ws = F >> 5, bs = F & 31;
+        for (int q = kLimbs - 1; q >= 0; --q) {
+            const int src = q - ws;
+            uint32_t hi = (src >= 0) ? N[src] : 0u;
+            uint32_t lo = (src - 1 >= 0) ? N[src - 1] : 0u;
+            N[q] = bs ? ((hi << bs) | (lo >> (32 - bs))) : hi;
+        }
+    }
+    // Q = N / cnt, remainder r  (cnt < 2^32)
+    uint32_t Q[kLimbs];
+    unsigned long long r = 0ull;
+    for (int q = kLimbs - 1; q >= 0; --q) {
+        const unsigned long long cur = (r << 32) | N[q];
+        Q[q] = (uint32_t)(cur / cnt);
+        r = cur % cnt;
+    }
+    int L = 0;
+    for (int q = kLimbs - 1; q >= 0; --q)
+        if (Q[q]) { L = 32 * q + (32 - __clz(Q[q])); break; }
+    int shift = L - 24;
+    if (shift < F) shift = F;  // subnormal result: LSB weight 2^-149
+    auto bit = [&](int i) -> uint32_t { return (i < 0) ? 0u : ((Q[i >> 5] >> (i & 31)) & 1u); };
+    uint32_t kept = 0u;
+    for (int i = 24; i >= 0; --i) kept = (kept << 1) | bit(shift + i);
+    const uint32_t round_bit = bit(shift - 1);
+    bool sticky = r != 0ull;
+    for (int i = 0; i < shift - 1 && !sticky; ++i) sticky = bit(i) != 0u;
+    if (round_bit && (sticky || (kept & 1u))) kept += 1u;
+    int ex = shift - 149 - F;  // value = kept * 2^ex
+    if (kept == (1u << 24)) { kept >>= 1; ex += 1; }
+    if (kept == 0u) return 0.0f;
+    uint32_t bits;
+    if (kept >= (1u << 23)) bits = ((uint32_t)(ex + 150) << 23) | (kept - (1u << 23));
+    else bits = kept;  // subnormal: ex == -149
+    return __uint_as_float(bits);
+}
+
+__global__ void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k, float* __restrict__ scales)
+{
+    const int axis = threadIdx.x;
+    if (axis >= 2) return;
+    const unsigned long long* g = ws + (int64_t)k * kStageWords;
+    scales[2 * k + axis] = exact_mean_f32(g + 256 * axis, g[kBuckets + axis]);
+}
+
+__global__ __launch_bounds__(kThreads) void k_pq_resid(const float* __restrict__ w_re,
+                                                       const float* __restrict__ w_im, int64_t count,
+                                                       int32_t stages, const float* __restrict__ scales,
+                                                       float* __restrict__ r_re, float* __restrict__ r_im)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float a = w_re[i], b = w_im[i];
+        for (int j = 0; j < stages; ++j) residual_step(a, b, phase_code(a, b), scales[2 * j], scales[2 * j + 1]);
+        if (r_re) r_re[i] = a;
+        if (r_im) r_im[i] = b;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Packing.  One thread per output word; reads the word's 16 codes as one
+// 16-byte load (m % 16 == 0, 16-byte aligned codes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t tiled_bit(int t) { return (t & 1) ? (uint32_t)(31 - t) : (uint32_t)(14 - t); }
+
+__device__ __forceinline__ void load16(const uint8_t* p, uint8_t out[16])
+{
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) out[t] = (uint8_t)(w[t >> 2] >> (8 * (t & 3)));
+}
+
+__global__ __launch_bounds__(kThreads) void k_pack(const uint8_t* __restrict__ codes, int32_t planes,
+                                                   int64_t rows, int64_t m, int32_t layout,
+                                                   uint32_t* __restrict__ out, int64_t nwords)
+{
+    const int64_t G = (m + 63) / 64;
+    for (int64_t wi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; wi < nwords;
+         wi += (int64_t)gridDim.x * blockDim.x) {
+        int64_t p, r, c0;
+        if (layout == FAIRY_LAYOUT_ROW16) {
+            const int64_t wpr = m / 16;
+            const int64_t pr = wi / wpr;
+            c0 = (wi - pr * wpr) * 16;
+            p = pr / rows;
+            r = pr - p * rows;
+        } else {
+            const int64_t u = wi & 3;
+            const int64_t q = wi >> 2;
+            p = q % planes;
+            const int64_t rg = q / planes;
+            const int64_t g = rg % G;
+            r = rg / G;
+            c0 = 64 * g + 16 * u;
+        }
+        uint32_t word = 0u;
+        if (c0 < m) {
+            uint8_t c[16];
+            load16(codes + (p * rows + r) * m + c0, c);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const uint32_t bitpos = (layout == FAIRY_LAYOUT_ROW16) ? (uint32_t)(2 * t) : tiled_bit(t);
+                word |= ((uint32_t)c[t] & 3u) << bitpos;
+            }
+        }
+        out[wi] = word;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_unpack(const uint32_t* __restrict__ in, int32_t planes,
+                                                     int64_t rows, int64_t m, int32_t layout,
+                                                     uint8_t* __restrict__ codes, int64_t nwords)
+{
+    const int64_t G = (m + 63) / 64;
+    for (int64_t wi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; wi < nwords;
+         wi += (int64_t)gridDim.x * blockDim.x) {
+        int64_t p, r, c0;
+        if (layout == FAIRY_LAYOUT_ROW16) {
+            const int64_t wpr = m / 16;
+            const int64_t pr = wi / wpr;
+            c0 = (wi - pr * wpr) * 16;
+            p = pr / rows;
+            r = pr - p * rows;
+        } else {
+            const int64_t u = wi & 3;
+            const int64_t q = wi >> 2;
+            p = q % planes;
+            const int64_t rg = q / planes;
+            const int64_t g = rg % G;
+            r = rg / G;
+            c0 = 64 * g + 16 * u;
+        }
+        if (c0 >= m) continue;
+        const uint32_t word = in[wi];
+        uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const uint32_t bitpos = (layout == FAIRY_LAYOUT_ROW16) ? (uint32_t)(2 * t) : tiled_bit(t);
+            o[t >> 2] |= ((word >> bitpos) & 3u) << (8 * (t & 3));
+        }
+        *reinterpret_cast<uint4*>(codes + (p * rows + r) * m + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_real_to_complex(const float* R, int64_t n, int64_t m, float* u_re, float* u_im,
+                                  float* w_re, float* w_im, hipStream_t s)
+{
+    const bool vec = (m % 4 == 0) && ((((uintptr_t)R) | ((uintptr_t)u_re) | ((uintptr_t)u_im) |
+                                       ((uintptr_t)w_re) | ((uintptr_t)w_im)) % 16 == 0);
+    const int64_t cols = vec ? m / 4 : m;
+    dim3 grid(grid_for(cols, kThreads, 64), (unsigned)(n < 65535 ? n : 65535));
+    if (vec)
+        hipLaunchKernelGGL(k_real_to_complex4, grid, dim3(kThreads), 0, s, (const float4*)R, n, m / 4,
+                           (float4*)u_re, (float4*)u_im, (float4*)w_re, (float4*)w_im);
+    else
+        hipLaunchKernelGGL(k_real_to_complex1, grid, dim3(kThreads), 0, s, R, n, m, u_re, u_im, w_re, w_im);
+    return hipGetLastError();
+}
+
+size_t phasequant_workspace_bytes(int32_t stages) { return (size_t)stages * kStageWords * sizeof(unsigned long long); }
+
+hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count, int32_t stages,
+                             uint8_t* codes, float* scales, float* resid_re, float* resid_im,
+                             void* workspace, hipStream_t s)
+{
+    unsigned long long* ws = (unsigned long long*)workspace;
+    const int64_t nws = (int64_t)stages * kStageWords;
+    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nws, kThreads, 64)), dim3(kThreads), 0, s, ws, nws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int grid = grid_for(count, kThreads, 2048);
+    for (int32_t k = 0; k < stages; ++k) {
+        hipLaunchKernelGGL(k_pq_stage, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, k,
+                           (const float*)scales, codes, ws);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_pq_finalize, dim3(1), dim3(64), 0, s, (const unsigned long long*)ws, k, scales);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (resid_re || resid_im) {
+        hipLaunchKernelGGL(k_pq_resid, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, stages,
+                           (const float*)scales, resid_re, resid_im);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+int64_t packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout)
+{
+    if (layout == FAIRY_LAYOUT_ROW16) return (int64_t)planes * rows * (m / 16);
+    return rows * ((m + 63) / 64) * planes * 4;
+}
+
+hipError_t launch_pack(const uint8_t* codes, int32_t planes, int64_t rows, int64_t m, int32_t layout,
+                       uint32_t* packed, hipStream_t s)
+{
+    const int64_t nw = packed_words(rows, m, planes, layout);
+    hipLaunchKernelGGL(k_pack, dim3(grid_for(nw, kThreads, 8192)), dim3(kThreads), 0, s, codes, planes, rows,
+                       m, layout, packed, nw);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint32_t* packed, int32_t planes, int64_t rows, int64_t m, int32_t layout,
+                         uint8_t* codes, hipStream_t s)
+{
+    const int64_t nw = packed_words(rows, m, planes, layout);
+    hipLaunchKernelGGL(k_unpack, dim3(grid_for(nw, kThreads, 8192)), dim3(kThreads), 0, s, packed, planes,
+                       rows, m, layout, codes, nw);
+    return hipGetLastError();
+}
+
+}  // namespace fairy

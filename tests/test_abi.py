@@ -1,0 +1,178 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/fairy.h declares,
+keep the oracle out of the product library, and reject invalid arguments on
+the host with the documented status before any launch (so these calls never
+reach the device).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from bit_complex_weight_amd import fairy as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fairy.h")
+
+A = 0x10000  # a 16-byte aligned fake device address: never dereferenced here
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(fairy_[a-z0-9_]+)\s*\(", txt)))
+
+
+def exported_symbols():
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+def test_library_loads():
+    assert F.fairy_abi_version() == 1
+
+
+def test_every_declared_entry_point_is_exported():
+    decl = declared_functions()
+    assert len(decl) >= 12, decl
+    syms = exported_symbols()
+    missing = [d for d in decl if d not in syms]
+    assert not missing, missing
+
+
+def test_oracle_not_linked_into_product():
+    syms = exported_symbols()
+    assert not any(s.startswith("orc_") for s in syms)
+    out = subprocess.run(["ldd", F.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out
+
+
+def test_status_strings():
+    seen = set()
+    for s in range(5):
+        t = F.status_string(s)
+        assert t and t not in seen
+        seen.add(t)
+    assert "UNKNOWN" in F.status_string(99)
+
+
+def test_packed_words():
+    assert F.fairy_packed_words(2048, 2048, 4, F.FAIRY_LAYOUT_TILED64) == 2048 * 32 * 4 * 4
+    assert F.fairy_packed_words(2048, 5504, 4, F.FAIRY_LAYOUT_TILED64) == 2048 * 86 * 4 * 4
+    assert F.fairy_packed_words(256, 256, 1, F.FAIRY_LAYOUT_ROW16) == 256 * 16
+    assert F.fairy_packed_words(10, 80, 2, F.FAIRY_LAYOUT_TILED64) == 10 * 2 * 2 * 4   # padded to 128 cols
+    assert F.fairy_packed_words(10, 24, 1, F.FAIRY_LAYOUT_ROW16) == -1                 # m % 16
+    assert F.fairy_packed_words(0, 16, 1, 0) == -1
+    assert F.fairy_packed_words(1, 16, 17, 0) == -1
+    assert F.fairy_packed_words(1, 16, 1, 7) == -1
+
+
+def test_workspace_sizes():
+    assert F.fairy_phasequant_workspace_bytes(1000, 2) == 2 * 514 * 8
+    assert F.fairy_phasequant_workspace_bytes(0, 2) == 0
+    assert F.fairy_phasequant_workspace_bytes(10, 9) == 0
+    assert F.fairy_phasequant_workspace_bytes(1 << 32, 1) == 0
+
+
+def status_of(fn, *args):
+    return fn(*args)
+
+
+L_ = F.lib()
+
+
+def test_real_to_complex_validation():
+    f = L_.fairy_real_to_complex
+    assert f(None, 2, 2, A, A, A, A, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, 0, 2, A, A, A, A, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, 2, -1, A, A, A, A, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A + 1, 2, 2, A, A, A, A, None) == F.FAIRY_ERR_INVALID_ARG
+
+
+def test_phasequant_validation():
+    f = L_.fairy_phasequant
+    ws = F.fairy_phasequant_workspace_bytes(100, 2)
+    assert f(None, A, 100, 2, A, A, None, None, A, ws, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 0, 2, A, A, None, None, A, ws, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 1 << 32, 2, A, A, None, None, A, ws, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 0, A, A, None, None, A, ws, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 9, A, A, None, None, A, ws, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 2, A, A + 2, None, None, A, ws, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 2, A, A, None, None, None, ws, None) == F.FAIRY_ERR_WORKSPACE
+    assert f(A, A, 100, 2, A, A, None, None, A, ws - 1, None) == F.FAIRY_ERR_WORKSPACE
+    assert f(A, A, 100, 2, A, A, None, None, A + 4, ws, None) == F.FAIRY_ERR_WORKSPACE
+
+
+def test_pack_validation():
+    for f in (L_.fairy_pack, L_.fairy_unpack):
+        assert f(None, 1, 4, 16, 0, A, None) == F.FAIRY_ERR_INVALID_ARG
+        assert f(A, 0, 4, 16, 0, A, None) == F.FAIRY_ERR_INVALID_ARG
+        assert f(A, 17, 4, 16, 0, A, None) == F.FAIRY_ERR_INVALID_ARG
+        assert f(A, 1, 0, 16, 0, A, None) == F.FAIRY_ERR_INVALID_ARG
+        assert f(A, 1, 4, 16, 2, A, None) == F.FAIRY_ERR_INVALID_ARG
+        assert f(A + 8, 1, 4, 16, 0, A, None) == F.FAIRY_ERR_INVALID_ARG
+        assert f(A, 1, 4, 24, 0, A, None) == F.FAIRY_ERR_UNSUPPORTED
+        assert f(A, 1, 4, 24, 1, A, None) == F.FAIRY_ERR_UNSUPPORTED
+
+
+def layer(**kw):
+    d = dict(n=64, m=64, stages=2, has_conj=1, layout=F.FAIRY_LAYOUT_TILED64, packed=A, scales=A)
+    d.update(kw)
+    return F.fairy_clinear(d["n"], d["m"], d["stages"], d["has_conj"], d["layout"], d["packed"], d["scales"])
+
+
+def gemv(Lr, xr=A, xi=A, dt=F.FAIRY_BF16, B=1, ldx=64, yr=A, yi=A, ldy=64, acc=None):
+    return L_.fairy_cgemv(ctypes.byref(Lr) if Lr is not None else None, xr, xi, dt, B, ldx, yr, yi, ldy, acc,
+                          None, 0, None)
+
+
+@pytest.mark.parametrize("kw,call,want", [
+    ({}, dict(B=0), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(B=65), F.FAIRY_ERR_INVALID_ARG),
+    ({"n": 0}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({"stages": 0}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({"stages": 9}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({"has_conj": 2}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({"layout": 5}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({"packed": None}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({"scales": None}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({"packed": A + 4}, {}, F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(xr=None), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(xi=A + 8), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(dt=3), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(ldx=48), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(ldx=72), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(ldy=63), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(yr=None), F.FAIRY_ERR_INVALID_ARG),
+    ({}, dict(acc=A), F.FAIRY_ERR_INVALID_ARG),            # acc only with I8
+    ({"layout": F.FAIRY_LAYOUT_ROW16}, {}, F.FAIRY_ERR_UNSUPPORTED),
+    ({"m": 72}, dict(ldx=80), F.FAIRY_ERR_UNSUPPORTED),     # m % 16
+    ({"m": 16400}, dict(ldx=16400), F.FAIRY_ERR_UNSUPPORTED),
+])
+def test_cgemv_validation(kw, call, want):
+    assert gemv(layer(**kw), **call) == want
+
+
+def test_cgemv_null_layer():
+    assert gemv(None) == F.FAIRY_ERR_INVALID_ARG
+
+
+def test_cgemm_validation():
+    f = L_.fairy_cgemm
+    Lr = layer()
+    args = lambda M=8, dt=F.FAIRY_BF16, algo=0, acc=None: (ctypes.byref(Lr), A, A, dt, M, 64, A, A, 64, acc, algo,
+                                                          None, 0, None)
+    assert f(*args(M=0)) == F.FAIRY_ERR_INVALID_ARG
+    assert f(*args(algo=3)) == F.FAIRY_ERR_INVALID_ARG
+    assert f(*args(acc=A)) == F.FAIRY_ERR_INVALID_ARG
+    assert f(*args(dt=F.FAIRY_F32, algo=F.FAIRY_ALGO_MFMA)) == F.FAIRY_ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_host_buffers():
+    import numpy as np
+    with pytest.raises(TypeError):
+        F._ptr(np.zeros(4))

@@ -1,0 +1,201 @@
+"""GPU parity of the complex GEMV / GEMM against the CPU oracle.
+
+Float activations: relative L2 error <= 1e-5 against the fp64 oracle on the
+same (bf16- or fp32-valued) inputs.  int8 activations: the int32
+accumulators equal the oracle's exact int64 sums.  Codes and scales of the
+end-to-end cases are produced on the GPU from the same seeded weights that
+the oracle quantises on the CPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_complex_weight_amd import fairy as F
+from bit_complex_weight_amd import synth
+from tests._gpu import (dev, host, layer_from_codes, log, quantize_widely_linear_on_gpu, rel_l2, run_gemv,
+                        torch)
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def x_bf16(B, m, seed):
+    re_b, im_b = synth.bf16_gaussian((B, m), seed)
+    return re_b, im_b, synth.bf16_to_f32(re_b), synth.bf16_to_f32(im_b)
+
+
+def check_float(layer, codes, scales, S, hc, B, xdtype, seed):
+    m = layer.m
+    if xdtype == F.FAIRY_BF16:
+        rb, ib, xr, xi = x_bf16(B, m, seed)
+        yr, yi, _ = run_gemv(layer, dev(rb), dev(ib), xdtype, B)
+    else:
+        xr, xi = synth.complex_gaussian((B, m), 1.0, seed)
+        yr, yi, _ = run_gemv(layer, dev(xr), dev(xi), xdtype, B)
+    wr, wi = oracle.cgemv_dense(codes, scales, S, hc, xr, xi)
+    err = rel_l2(yr + 1j * yi, wr + 1j * wi)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
+    return yr, yi
+
+
+# --- the 256x256 single GEMV: one stage, no conjugate branch ----------------------
+def test_c1_single_gemv_f32_and_i8():
+    log("256x256 S=1 no-conj f32 + i8")
+    re, im = synth.complex_gaussian((256, 256), 1.0, 0)
+    codes, scales, _, _ = oracle.phasequant(re, im, 1, want_resid=False)
+    layer = layer_from_codes(codes, scales, 1, False)
+    check_float(layer, codes, scales, 1, False, 1, F.FAIRY_F32, 1)
+    xr, xi = synth.int8_uniform((1, 256), 2)
+    yr, yi, acc = run_gemv(layer, dev(xr), dev(xi), F.FAIRY_I8, 1, want_acc=True)
+    want = oracle.cgemv_acc_i64(codes, xr, xi)
+    assert np.array_equal(acc.astype(np.int64), want)
+    wr, wi = oracle.cgemv_dense(codes, scales, 1, False, xr.astype(np.float64), xi.astype(np.float64))
+    assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
+
+
+# --- random codes: shapes, tails, plane counts, batch sizes ------------------------
+CASES = [
+    # (S, has_conj, n, m, B)
+    (1, False, 1, 16, 1),
+    (1, True, 5, 64, 2),
+    (2, True, 37, 80, 3),        # ragged rows and a half-empty column group
+    (3, True, 64, 208, 5),
+    (2, False, 100, 1024, 8),
+    (4, True, 9, 128, 9),        # P = 8
+    (8, True, 3, 64, 2),         # P = 16
+    (2, True, 130, 2048, 16),
+    (2, True, 64, 5504, 4),
+    (1, True, 20, 256, 64),
+]
+
+
+@pytest.mark.parametrize("S,hc,n,m,B", CASES)
+@pytest.mark.parametrize("xdtype", [F.FAIRY_BF16, F.FAIRY_F32])
+def test_gemv_float_random_codes(S, hc, n, m, B, xdtype):
+    log(f"gemv float S={S} conj={hc} n={n} m={m} B={B} dt={xdtype}")
+    P = S * (2 if hc else 1)
+    codes = synth.random_codes((P, n, m), 7 * n + m)
+    scales = synth.random_scales(P, n + 3 * m)
+    layer = layer_from_codes(codes, scales, S, hc)
+    check_float(layer, codes, scales, S, hc, B, xdtype, 11 + B)
+
+
+@pytest.mark.parametrize("S,hc,n,m,B", CASES)
+def test_gemv_i8_exact(S, hc, n, m, B):
+    log(f"gemv i8 S={S} conj={hc} n={n} m={m} B={B}")
+    P = S * (2 if hc else 1)
+    codes = synth.random_codes((P, n, m), 5 * n + m)
+    scales = synth.random_scales(P, n + m)
+    layer = layer_from_codes(codes, scales, S, hc)
+    xr, xi = synth.int8_uniform((B, m), 3 + B)
+    yr, yi, acc = run_gemv(layer, dev(xr), dev(xi), F.FAIRY_I8, B, want_acc=True)
+    assert np.array_equal(acc.astype(np.int64), oracle.cgemv_acc_i64(codes, xr, xi))
+    wr, wi = oracle.cgemv_dense(codes, scales, S, hc, xr.astype(np.float64), xi.astype(np.float64))
+    assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
+
+
+def test_gemv_extreme_int8_values():
+    """All-(+-127) activations and all-equal codes: the largest exact sums."""
+    S, n, m = 2, 8, 2048
+    for c in range(4):
+        codes = np.full((2 * S, n, m), c, np.uint8)
+        layer = layer_from_codes(codes, np.ones((2 * S, 2), np.float32), S, True)
+        for v in (127, -127):
+            xr = np.full((2, m), v, np.int8); xi = np.full((2, m), -v, np.int8)
+            _, _, acc = run_gemv(layer, dev(xr), dev(xi), F.FAIRY_I8, 2, want_acc=True)
+            assert np.array_equal(acc.astype(np.int64), oracle.cgemv_acc_i64(codes, xr, xi))
+
+
+def test_gemv_deterministic():
+    codes = synth.random_codes((4, 256, 2048), 1)
+    scales = synth.random_scales(4, 2)
+    layer = layer_from_codes(codes, scales, 2, True)
+    rb, ib, _, _ = x_bf16(4, 2048, 3)
+    a = run_gemv(layer, dev(rb), dev(ib), F.FAIRY_BF16, 4)
+    b = run_gemv(layer, dev(rb), dev(ib), F.FAIRY_BF16, 4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_gemv_respects_strides():
+    """ldx > m and ldy > n: padding columns/rows are neither read nor written."""
+    t = torch()
+    S, n, m, B = 1, 40, 64, 3
+    codes = synth.random_codes((2, n, m), 4)
+    scales = synth.random_scales(2, 5)
+    layer = layer_from_codes(codes, scales, S, True)
+    xr, xi = synth.complex_gaussian((B, m), 1.0, 6)
+    ldx, ldy = 96, 50
+    Xr = np.full((B, ldx), np.nan, np.float32); Xr[:, :m] = xr
+    Xi = np.full((B, ldx), np.nan, np.float32); Xi[:, :m] = xi
+    yr = t.full((B, ldy), 7.0, device="cuda"); yi = t.full((B, ldy), 7.0, device="cuda")
+    F.fairy_cgemv(layer.desc, dev(Xr), dev(Xi), F.FAIRY_F32, B, ldx, yr, yi, ldy)
+    t.cuda.synchronize()
+    yr, yi = host(yr), host(yi)
+    assert np.all(yr[:, n:] == 7.0) and np.all(yi[:, n:] == 7.0)
+    wr, wi = oracle.cgemv_dense(codes, scales, S, True, xr, xi)
+    assert rel_l2(yr[:, :n] + 1j * yi[:, :n], wr + 1j * wi) <= TOL
+
+
+# --- LLaMA-2-7B-shaped widely-linear layers, quantised on the GPU -------------------
+def widely_linear_case(rows, cols, seed, S):
+    """Real [rows][cols] sigma=0.02 -> complex U, W [rows/2][cols/2] -> S stages,
+    on the GPU; the oracle does the same on the CPU."""
+    t = torch()
+    n, m = rows // 2, cols // 2
+    R = synth.real_layer(rows, cols, seed)
+    planes = [t.empty((n, m), dtype=t.float32, device="cuda") for _ in range(4)]
+    F.fairy_real_to_complex(dev(R), n, m, *planes)
+    layer, gcodes, gscales = quantize_widely_linear_on_gpu(*planes, n, m, S)
+    ur, ui, wr, wi = oracle.real_to_complex(R, n, m, f32=True)
+    cu, su, _, _ = oracle.phasequant(ur, ui, S, want_resid=False)
+    cw, sw, _, _ = oracle.phasequant(wr, wi, S, want_resid=False)
+    codes = np.concatenate([cu, cw])
+    scales = np.concatenate([su, sw])
+    t.cuda.synchronize()
+    assert np.array_equal(host(gcodes).reshape(codes.shape), codes)
+    assert np.array_equal(host(gscales).reshape(scales.shape).view(np.uint32), scales.view(np.uint32))
+    return layer, codes, scales
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_llama_attention_shape_s2(B):
+    log(f"widely-linear 4096x4096 -> 2048x2048 S=2 B={B}")
+    layer, codes, scales = widely_linear_case(4096, 4096, 200, 2)
+    check_float(layer, codes, scales, 2, True, B, F.FAIRY_BF16, 201)
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(11008, 4096, 300), (4096, 11008, 302)])
+@pytest.mark.parametrize("B", [1, 8])
+def test_llama_mlp_shapes_s2(rows, cols, seed, B):
+    log(f"widely-linear {rows}x{cols} S=2 B={B}")
+    layer, codes, scales = widely_linear_case(rows, cols, seed, 2)
+    check_float(layer, codes, scales, 2, True, B, F.FAIRY_BF16, seed + 1)
+
+
+# --- prefill GEMM (sampled outputs) ---------------------------------------------------
+@pytest.mark.parametrize("xdtype", [F.FAIRY_BF16, F.FAIRY_I8])
+def test_prefill_gemm_sampled(xdtype):
+    log(f"prefill M=2048 2048x2048 S=2 dt={xdtype} (VALU)")
+    S, n, m, M = 2, 2048, 2048, 2048
+    codes = synth.random_codes((2 * S, n, m), 400)
+    scales = synth.random_scales(2 * S, 401)
+    layer = layer_from_codes(codes, scales, S, True)
+    if xdtype == F.FAIRY_BF16:
+        rb, ib = synth.bf16_gaussian((M, m), 402)
+        xr, xi = synth.bf16_to_f32(rb), synth.bf16_to_f32(ib)
+        yr, yi, _ = run_gemv(layer, dev(rb), dev(ib), xdtype, M, gemm=True, algo=F.FAIRY_ALGO_VALU)
+    else:
+        xr, xi = synth.int8_uniform((M, m), 403)
+        yr, yi, acc = run_gemv(layer, dev(xr), dev(xi), xdtype, M, want_acc=True, gemm=True,
+                               algo=F.FAIRY_ALGO_VALU)
+    g = synth.rng(404)
+    rows = np.sort(g.choice(n, 48, replace=False))
+    toks = np.sort(g.choice(M, 48, replace=False))
+    wr, wi = oracle.cgemv_dense(codes[:, rows], scales, S, True, xr[toks].astype(np.float64),
+                                xi[toks].astype(np.float64))
+    got = yr[np.ix_(toks, rows)] + 1j * yi[np.ix_(toks, rows)]
+    assert rel_l2(got, wr + 1j * wi) <= TOL
+    if xdtype == F.FAIRY_I8:
+        want_acc = oracle.cgemv_acc_i64(codes[:, rows], xr[toks], xi[toks])
+        assert np.array_equal(acc[:, :, toks][:, :, :, rows].astype(np.int64), want_acc)
