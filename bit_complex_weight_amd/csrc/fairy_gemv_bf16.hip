@@ -1,0 +1,8 @@
+// fairy_gemv_bf16.hip -- bf16-activation GEMV kernels (v_dot2_f32_bf16).
+#include "fairy_gemv_impl.h"
+
+namespace fairy {
+namespace gemv {
+hipError_t launch_bf16(const GemvArgs& a, hipStream_t s) { return launch_float<FAIRY_BF16>(a, s); }
+}  // namespace gemv
+}  // namespace fairy

@@ -1,0 +1,426 @@
+// fairy_gemv_impl.h -- kernels of the decode-time complex GEMV (internal).
+//
+//   y[b] = sum_k What(U_k) x[b] + sum_k What(W_k) conj(x[b])     [Fairy2i article §4.2, §2.1]
+//
+// Multiplication-free form: per plane, row and batch column four fp32 sums
+//   A1 = sum ReB x_re,  A2 = sum ImB x_im,  A3 = sum ReB x_im,  A4 = sum ImB x_re
+// with ReB, ImB in {-1, 0, 1} ([iFairy abstract]: one non-zero axis per code;
+// [iFairy talk §2.3.1]: times i is a swap and a negation), and the per-axis
+// scales applied once per plane in the epilogue:
+//   U plane: y_re += s_re A1 - s_im A2,  y_im += s_re A3 + s_im A4
+//   W plane: y_re += s_re A1 + s_im A2,  y_im += s_im A4 - s_re A3
+//
+// Work mapping (wave64).  A row's packed data in TILED64 is G*P contiguous
+// 16-byte units (group g of 64 columns, plane p).  TROW consecutive lanes
+// own a row; lane l takes units l, l+TROW, ... so every load instruction of
+// a wave reads consecutive 16-byte units (fully coalesced, 1 KiB per wave
+// when TROW = 64).  The lane's first units are loaded before the block stages
+// the activations into LDS, so HBM latency overlaps the staging.  Per unit a
+// lane decodes 64 codes with bit operations (decode_bf16_pair), multiplies
+// nothing, accumulates A1..A4 with v_dot2_f32_bf16 (bf16) or fp32 FMAs on the
+// +-2 / 0 decoded values (fp32), and folds the plane's scales in once.  Row
+// partial sums are combined across the TROW lanes with DPP / ds_swizzle
+// butterflies: deterministic, no atomics.
+#pragma once
+
+#include "fairy_internal.h"
+
+namespace fairy {
+namespace gemv {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+
+struct GemvArgs {
+    const uint32_t* packed;
+    const float* scales;
+    const void* x_re;
+    const void* x_im;
+    float* y_re;
+    float* y_im;
+    int32_t* acc;
+    int64_t ldx, ldy;
+    int32_t n, m, m64, G, S, P, B;
+};
+
+constexpr int kThreads = 256;
+constexpr int kScaleBytes = 128;  // LDS prefix holding up to 16 planes x 2 half-scales
+
+// Staged activations are stored per 64-column group with 16 bytes of padding
+// after each group: lanes of a wave read different groups, and without the
+// pad all groups would start on the same LDS banks (group stride a multiple
+// of 128 B), serialising every 128-bit read.
+__host__ __device__ inline int x_esize(int xdtype) { return xdtype == FAIRY_F32 ? 4 : xdtype == FAIRY_BF16 ? 2 : 1; }
+__host__ __device__ inline int x_group_bytes(int xdtype) { return 64 * x_esize(xdtype) + 16; }
+__host__ __device__ inline int x_plane_bytes(int xdtype, int m64) { return (m64 / 64) * x_group_bytes(xdtype); }
+// bytes of LDS one staged batch column occupies (re + im planes)
+__host__ __device__ inline int x_bytes_per_col(int xdtype, int m64) { return 2 * x_plane_bytes(xdtype, m64); }
+// byte offset of column c inside a staged plane
+__device__ __forceinline__ int x_col_off(int xdtype, int c)
+{
+    return (c >> 6) * x_group_bytes(xdtype) + (c & 63) * x_esize(xdtype);
+}
+
+// ---------------------------------------------------------------------------
+// Activation staging into LDS.  Per batch column b of the chunk:
+//   bf16: re plane [m64] then im plane [m64] (uint16)
+//   f32 : re [m64], im [m64] (float)
+//   i8  : re [m64], im [m64] bytes; inside every 16-column word the bytes are
+//         reordered to the four dot4 groups (see i8_group_col).
+// Columns >= m are zero.
+// ---------------------------------------------------------------------------
+template <int XT>
+__device__ __forceinline__ void stage_x(const GemvArgs& a, int b0, int nb, uint8_t* lds)
+{
+    constexpr int per_elems = (XT == FAIRY_BF16) ? 8 : (XT == FAIRY_F32) ? 4 : 16;  // elements per 16 B
+    constexpr int esize = 16 / per_elems;
+    const int per = a.m64 / per_elems;
+    const int pbytes = x_plane_bytes(XT, a.m64);
+    for (int idx = threadIdx.x; idx < nb * 2 * per; idx += blockDim.x) {
+        const int b = idx / (2 * per);
+        const int rem = idx - b * 2 * per;
+        const int plane = rem / per;
+        const int c = (rem - plane * per) * per_elems;
+        uint4* dst = reinterpret_cast<uint4*>(lds + (size_t)(2 * b + plane) * pbytes + x_col_off(XT, c));
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(plane ? a.x_im : a.x_re) +
+                             ((int64_t)(b0 + b) * a.ldx + c) * esize;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (c < a.m) v = *reinterpret_cast<const uint4*>(src);
+        if constexpr (XT == FAIRY_I8) {
+            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+            uint32_t out[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                uint32_t o = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) {
+                    const int t = i8_group_col(s, bb);
+                    o |= ((in[t >> 2] >> (8 * (t & 3))) & 0xFFu) << (8 * bb);
+                }
+                out[s] = o;
+            }
+            v = make_uint4(out[0], out[1], out[2], out[3]);
+        }
+        *dst = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Float paths (bf16 / fp32 activations), one 16-byte unit (64 codes of one
+// plane) at a time.
+// ---------------------------------------------------------------------------
+template <int XT, int BCH>
+__device__ __forceinline__ void unit_accumulate(const uint4 cw, int col0, const uint8_t* xs, int col_bytes,
+                                                int plane_bytes, int nb, float (&A)[4][BCH])
+{
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t w = words[u];
+        const int c0 = col0 + 16 * u;
+        if constexpr (XT == FAIRY_BF16) {
+            uint32_t re2[8], im2[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) decode_bf16_pair(w, k, re2[k], im2[k]);
+#pragma unroll
+            for (int b = 0; b < BCH; ++b) {
+                if (b >= nb) continue;
+                const uint8_t* xb = xs + (size_t)b * col_bytes + x_col_off(FAIRY_BF16, c0);
+                const uint4 r0 = *reinterpret_cast<const uint4*>(xb);
+                const uint4 r1 = *reinterpret_cast<const uint4*>(xb + 16);
+                const uint4 i0 = *reinterpret_cast<const uint4*>(xb + plane_bytes);
+                const uint4 i1 = *reinterpret_cast<const uint4*>(xb + plane_bytes + 16);
+                const uint32_t xr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+                const uint32_t xi[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    A[0][b] = dot2_bf16(re2[k], xr[k], A[0][b]);
+                    A[2][b] = dot2_bf16(re2[k], xi[k], A[2][b]);
+                    A[1][b] = dot2_bf16(im2[k], xi[k], A[1][b]);
+                    A[3][b] = dot2_bf16(im2[k], xr[k], A[3][b]);
+                }
+            }
+        } else {
+            float re[16], im[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const uint32_t ws = w << f32_shift(t);
+                im[t] = __uint_as_float(ws & 0xC0000000u);
+                re[t] = __uint_as_float((ws ^ 0x40000000u) & 0xC0000000u);
+            }
+#pragma unroll
+            for (int b = 0; b < BCH; ++b) {
+                if (b >= nb) continue;
+                const float* xr = reinterpret_cast<const float*>(xs + (size_t)b * col_bytes + x_col_off(FAIRY_F32, c0));
+                const float* xi = reinterpret_cast<const float*>(xs + (size_t)b * col_bytes + plane_bytes +
+                                                                 x_col_off(FAIRY_F32, c0));
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    const float vr = xr[t], vi = xi[t];
+                    A[0][b] = fmaf(re[t], vr, A[0][b]);
+                    A[2][b] = fmaf(re[t], vi, A[2][b]);
+                    A[1][b] = fmaf(im[t], vi, A[1][b]);
+                    A[3][b] = fmaf(im[t], vr, A[3][b]);
+                }
+            }
+        }
+    }
+}
+
+template <int XT, int TROW, int BCH, int UB>
+__global__ __launch_bounds__(kThreads) void k_cgemv_units(GemvArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    float* s_hs = reinterpret_cast<float*>(lds);        // [P][2] half-scales (decoded weights are +-2)
+    uint8_t* xs = lds + kScaleBytes;
+    const int lr = threadIdx.x % TROW;
+    const int row = blockIdx.x * (kThreads / TROW) + threadIdx.x / TROW;
+    const bool row_ok = row < a.n;
+    const int P = a.P;
+    const int units = a.G * P;
+    const int nmine = (row_ok && lr < units) ? (units - lr + TROW - 1) / TROW : 0;
+    const uint4* wrow = reinterpret_cast<const uint4*>(a.packed) + (int64_t)(row_ok ? row : 0) * units;
+    // unit j = lr + k*TROW -> (group, plane), advanced without divisions
+    const int dq = TROW / P, dr = TROW - dq * P;
+    const int g_first = lr / P, p_first = lr - g_first * P;
+
+    // issue the first batch of weight loads before anything else
+    uint4 cw[UB];
+#pragma unroll
+    for (int k = 0; k < UB; ++k) cw[k] = (k < nmine) ? wrow[lr + k * TROW] : make_uint4(0, 0, 0, 0);
+
+    if (threadIdx.x < 2 * P) s_hs[threadIdx.x] = 0.5f * a.scales[threadIdx.x];
+    const int col_bytes = x_bytes_per_col(XT, a.m64);
+    const int plane_bytes = col_bytes / 2;
+
+    for (int b0 = 0; b0 < a.B; b0 += BCH) {
+        const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
+        if (b0) {
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < UB; ++k) cw[k] = (k < nmine) ? wrow[lr + k * TROW] : make_uint4(0, 0, 0, 0);
+        }
+        stage_x<XT>(a, b0, nb, xs);
+        __syncthreads();
+
+        float yr[BCH], yi[BCH];
+#pragma unroll
+        for (int b = 0; b < BCH; ++b) { yr[b] = 0.f; yi[b] = 0.f; }
+
+        int g = g_first, p = p_first;
+        for (int kb = 0; kb < nmine; kb += UB) {
+            if (kb) {
+#pragma unroll
+                for (int k = 0; k < UB; ++k)
+                    cw[k] = (kb + k < nmine) ? wrow[lr + (kb + k) * TROW] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < UB; ++k) {
+                if (kb + k < nmine) {
+                    float A[4][BCH];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int b = 0; b < BCH; ++b) A[q][b] = 0.f;
+                    unit_accumulate<XT, BCH>(cw[k], 64 * g, xs, col_bytes, plane_bytes, nb, A);
+                    const float hr = s_hs[2 * p], hi = s_hs[2 * p + 1];
+                    const float sg = (p < a.S) ? 1.0f : -1.0f;  // W planes multiply conj(x)
+#pragma unroll
+                    for (int b = 0; b < BCH; ++b) {
+                        yr[b] += hr * A[0][b] - sg * (hi * A[1][b]);
+                        yi[b] += sg * (hr * A[2][b]) + hi * A[3][b];
+                    }
+                }
+                g += dq;
+                p += dr;
+                if (p >= P) { p -= P; ++g; }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < BCH; ++b) {
+            const float sr = group_sum<TROW>(yr[b]);
+            const float si = group_sum<TROW>(yi[b]);
+            if (lr == 0 && row_ok && b < nb) {
+                a.y_re[(int64_t)(b0 + b) * a.ldy + row] = sr;
+                a.y_im[(int64_t)(b0 + b) * a.ldy + row] = si;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// int8 path: exact int32 accumulators per plane, reduced across lanes, then
+// the float epilogue from the exact sums.  A lane owns whole 64-column groups
+// (all planes), so its per-plane sums stay in registers.
+// v_perm tables (pool bytes 0..3 from the second operand, 4..7 from the first;
+// selector 8 replicates bit 15, 9 bit 31, 12 gives 0x00, 13.. give 0xFF):
+//   codes at byte bits 1:0 -> selector c:    ReB pool 01 00 FF 00, ImB pool 00 01 00 FF
+//   codes at byte bits 3:2 -> selector 4c:   ReB: c=0 byte0=01, c=1 byte4=00,
+//                                            c=2 sign(bit15)=FF, c=3 -> 00
+//                           selector 4c|1:   ImB: c=0 byte1=00, c=1 byte5=01,
+//                                            c=2 sign(bit31)=00, c=3 -> FF
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void ternary_bytes(uint32_t w, uint32_t (&re)[4], uint32_t (&im)[4])
+{
+    const uint32_t w4 = w >> 4;
+    const uint32_t s0 = w & 0x03030303u;
+    const uint32_t s2 = w4 & 0x03030303u;
+    const uint32_t s1r = w & 0x0C0C0C0Cu, s1i = s1r | 0x01010101u;
+    const uint32_t s3r = w4 & 0x0C0C0C0Cu, s3i = s3r | 0x01010101u;
+    re[0] = __builtin_amdgcn_perm(0u, 0x00FF0001u, s0);
+    im[0] = __builtin_amdgcn_perm(0u, 0xFF000100u, s0);
+    re[1] = __builtin_amdgcn_perm(0u, 0x00008001u, s1r);
+    im[1] = __builtin_amdgcn_perm(0x00000100u, 0u, s1i);
+    re[2] = __builtin_amdgcn_perm(0u, 0x00FF0001u, s2);
+    im[2] = __builtin_amdgcn_perm(0u, 0xFF000100u, s2);
+    re[3] = __builtin_amdgcn_perm(0u, 0x00008001u, s3r);
+    im[3] = __builtin_amdgcn_perm(0x00000100u, 0u, s3i);
+}
+
+template <int PMAX, int TROW, int BCH>
+__global__ __launch_bounds__(kThreads) void k_cgemv_i8(GemvArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t* xs = lds + kScaleBytes;
+    const int rows_pb = kThreads / TROW;
+    const int lr = threadIdx.x % TROW;
+    const int row = blockIdx.x * rows_pb + threadIdx.x / TROW;
+    const bool row_ok = row < a.n;
+    const int P = a.P;
+    const uint4* wrow = reinterpret_cast<const uint4*>(a.packed) + (int64_t)(row_ok ? row : 0) * a.G * P;
+    const int plane_bytes = x_plane_bytes(FAIRY_I8, a.m64);
+
+    for (int b0 = 0; b0 < a.B; b0 += BCH) {
+        const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
+        if (b0) __syncthreads();
+        stage_x<FAIRY_I8>(a, b0, nb, xs);
+        __syncthreads();
+
+        int A[PMAX][4][BCH];
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int b = 0; b < BCH; ++b) A[p][q][b] = 0;
+
+        for (int g = lr; g < a.G; g += TROW) {
+            uint4 cw[PMAX];
+#pragma unroll
+            for (int p = 0; p < PMAX; ++p)
+                cw[p] = (p < P && row_ok) ? wrow[(int64_t)g * P + p] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int col0 = 64 * g + 16 * u;
+                uint4 xr4[BCH], xi4[BCH];
+#pragma unroll
+                for (int b = 0; b < BCH; ++b) {
+                    const uint8_t* xb = xs + (size_t)b * 2 * plane_bytes + x_col_off(FAIRY_I8, col0);
+                    xr4[b] = *reinterpret_cast<const uint4*>(xb);
+                    xi4[b] = *reinterpret_cast<const uint4*>(xb + plane_bytes);
+                }
+#pragma unroll
+                for (int p = 0; p < PMAX; ++p) {
+                    if (p >= P) continue;
+                    const uint32_t w = (u == 0) ? cw[p].x : (u == 1) ? cw[p].y : (u == 2) ? cw[p].z : cw[p].w;
+                    uint32_t re[4], im[4];
+                    ternary_bytes(w, re, im);
+#pragma unroll
+                    for (int b = 0; b < BCH; ++b) {
+                        const uint32_t xr[4] = {xr4[b].x, xr4[b].y, xr4[b].z, xr4[b].w};
+                        const uint32_t xi[4] = {xi4[b].x, xi4[b].y, xi4[b].z, xi4[b].w};
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            A[p][0][b] = __builtin_amdgcn_sdot4((int)re[s], (int)xr[s], A[p][0][b], false);
+                            A[p][1][b] = __builtin_amdgcn_sdot4((int)im[s], (int)xi[s], A[p][1][b], false);
+                            A[p][2][b] = __builtin_amdgcn_sdot4((int)re[s], (int)xi[s], A[p][2][b], false);
+                            A[p][3][b] = __builtin_amdgcn_sdot4((int)im[s], (int)xr[s], A[p][3][b], false);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < BCH; ++b) {
+            float yr = 0.f, yi = 0.f;
+#pragma unroll
+            for (int p = 0; p < PMAX; ++p) {
+                if (p >= P) continue;
+                int t[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) t[q] = group_sum_i<TROW>(A[p][q][b]);
+                if (lr == 0 && row_ok && b < nb) {
+                    if (a.acc) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            a.acc[(((int64_t)p * 4 + q) * a.B + (b0 + b)) * a.n + row] = t[q];
+                    }
+                    const float s_re = a.scales[2 * p], s_im = a.scales[2 * p + 1];
+                    const float f1 = (float)t[0], f2 = (float)t[1], f3 = (float)t[2], f4 = (float)t[3];
+                    if (p < a.S) {
+                        yr += s_re * f1 - s_im * f2;
+                        yi += s_re * f3 + s_im * f4;
+                    } else {
+                        yr += s_re * f1 + s_im * f2;
+                        yi += s_im * f4 - s_re * f3;
+                    }
+                }
+            }
+            if (lr == 0 && row_ok && b < nb) {
+                a.y_re[(int64_t)(b0 + b) * a.ldy + row] = yr;
+                a.y_im[(int64_t)(b0 + b) * a.ldy + row] = yi;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers (instantiated per activation type in its own
+// translation unit so the kernels compile in parallel)
+// ---------------------------------------------------------------------------
+int pick_trow(int units);
+int pick_bch(int xdtype, int B, int m64);
+
+template <int XT, int TROW, int BCH>
+hipError_t launch_units_t(const GemvArgs& a, hipStream_t s)
+{
+    const dim3 grid((a.n + (kThreads / TROW) - 1) / (kThreads / TROW));
+    const size_t lds = kScaleBytes + (size_t)x_bytes_per_col(XT, a.m64) * BCH;
+    hipLaunchKernelGGL((k_cgemv_units<XT, TROW, BCH, 2>), grid, dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int XT, int TROW>
+hipError_t launch_units_bch(const GemvArgs& a, int bch, hipStream_t s)
+{
+    switch (bch) {
+    case 8: return launch_units_t<XT, TROW, 8>(a, s);
+    case 4: return launch_units_t<XT, TROW, 4>(a, s);
+    case 2: return launch_units_t<XT, TROW, 2>(a, s);
+    default: return launch_units_t<XT, TROW, 1>(a, s);
+    }
+}
+
+template <int XT>
+hipError_t launch_float(const GemvArgs& a, hipStream_t s)
+{
+    const int bch = pick_bch(XT, a.B, a.m64);
+    switch (pick_trow(a.G * a.P)) {
+    case 64: return launch_units_bch<XT, 64>(a, bch, s);
+    case 32: return launch_units_bch<XT, 32>(a, bch, s);
+    case 16: return launch_units_bch<XT, 16>(a, bch, s);
+    default: return launch_units_bch<XT, 8>(a, bch, s);
+    }
+}
+
+hipError_t launch_bf16(const GemvArgs& a, hipStream_t s);
+hipError_t launch_f32(const GemvArgs& a, hipStream_t s);
+hipError_t launch_i8(const GemvArgs& a, hipStream_t s);
+
+}  // namespace gemv
+}  // namespace fairy

@@ -116,20 +116,9 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t count)
         p[i] = 0ull;
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
-{
-    v += (uint32_t)__shfl_xor((int)v, 1);
-    v += (uint32_t)__shfl_xor((int)v, 2);
-    v += (uint32_t)__shfl_xor((int)v, 4);
-    v += (uint32_t)__shfl_xor((int)v, 8);
-    v += (uint32_t)__shfl_xor((int)v, 16);
-    v += (uint32_t)__shfl_xor((int)v, 32);
-    return v;
-}
-
 // Stage k: recompute R_k from W with the scales of stages < k (already on
 // the device), write code_k, and add |R_k| on the code's axis into the
-// stage's exponent buckets.
+// stage's exponent buckets (block-local LDS buckets, flushed once per block).
 __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__ w_re,
                                                        const float* __restrict__ w_im, int64_t count,
                                                        int32_t k, const float* __restrict__ scales,
@@ -147,32 +136,26 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
     for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < count; base += stride) {
         const int64_t i = base + threadIdx.x;
         const bool valid = i < count;
-        int key = 0;
-        uint32_t sig = 0;
+        uint32_t axis = 0;
         if (valid) {
             float a = w_re[i], b = w_im[i];
             for (int j = 0; j < k; ++j) residual_step(a, b, phase_code(a, b), scales[2 * j], scales[2 * j + 1]);
             const uint32_t c = phase_code(a, b);
             codes[(int64_t)k * count + i] = (uint8_t)c;
-            const uint32_t axis = c & 1u;
+            axis = c & 1u;
             const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
             const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
-            sig = ex ? (man | 0x800000u) : man;
-            key = (int)(axis * 256u + (ex ? ex : 1u));
+            const uint32_t sig = ex ? (man | 0x800000u) : man;
+            if (sig) atomicAdd(&s_buck[axis * 256u + (ex ? ex : 1u)], (unsigned long long)sig);
         }
-        // aggregate equal keys across the wave, one LDS atomic per key
-        unsigned long long pending = __ballot(valid);
-        while (pending) {
-            const int leader = __ffsll((long long)pending) - 1;
-            const int k0 = __shfl(key, leader);
-            const bool mine = valid && key == k0;
-            const unsigned long long same = __ballot(mine);
-            const uint32_t tot = wave_sum_u32(mine ? sig : 0u);
-            if (lane == leader) {
-                atomicAdd(&s_buck[k0], (unsigned long long)tot);
-                atomicAdd(&s_cnt[k0 >> 8], (unsigned long long)__popcll(same));
-            }
-            pending &= ~same;
+        // counts per axis: one ballot per wave instead of per-element atomics
+        const unsigned long long im_mask = __ballot(valid && axis == 1u);
+        const unsigned long long all_mask = __ballot(valid);
+        if (lane == 0) {
+            const unsigned long long n_im = __popcll(im_mask);
+            const unsigned long long n_all = __popcll(all_mask);
+            if (n_all - n_im) atomicAdd(&s_cnt[0], n_all - n_im);
+            if (n_im) atomicAdd(&s_cnt[1], n_im);
         }
     }
     __syncthreads();
@@ -182,85 +165,102 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
     if (threadIdx.x < 2 && s_cnt[threadIdx.x]) atomicAdd(&g[kBuckets + threadIdx.x], s_cnt[threadIdx.x]);
 }
 
-// Exact mean -> fp32, nearest even.  N = sum_eb bucket[eb] * 2^(eb-1) is the
-// sum in units of 2^-149; the mean is N / cnt * 2^-149.  Long division yields
-// a quotient with >= 25 significant bits; the bits below the fp32 significand
-// plus the remainder give the round and sticky information.
-constexpr int kLimbs = 13;  // 416 bits: N < 2^(254 + 54)
-
-__device__ float exact_mean_f32(const unsigned long long* __restrict__ buck, unsigned long long cnt)
-{
-    if (cnt == 0ull) return 0.0f;
-    uint32_t N[kLimbs];
-    for (int i = 0; i < kLimbs; ++i) N[i] = 0u;
-    for (int eb = 1; eb < 256; ++eb) {
-        const unsigned long long v = buck[eb];
-        if (!v) continue;
-        const int pos = eb - 1, wi = pos >> 5, sh = pos & 31;
-        uint32_t part[3];
-        part[0] = (uint32_t)(v << sh);
-        part[1] = (uint32_t)(sh ? (v >> (32 - sh)) : (v >> 32));
-        part[2] = (uint32_t)(sh ? (v >> (64 - sh)) : 0ull);
-        unsigned long long carry = 0ull;
-        for (int q = wi; q < kLimbs; ++q) {
-            const unsigned long long add = (q - wi < 3) ? part[q - wi] : 0u;
-            const unsigned long long s = (unsigned long long)N[q] + add + carry;
-            N[q] = (uint32_t)s;
-            carry = s >> 32;
-        }
-    }
-    int T = 0;  // bit length of N
-    for (int q = kLimbs - 1; q >= 0; --q)
-        if (N[q]) { T = 32 * q + (32 - __clz(N[q])); break; }
-    if (T == 0) return 0.0f;
-    const int Lc = 64 - __clzll(cnt);
-    int F = 27 + Lc - T;
-    if (F < 0) F = 0;
-    // N <<= F
-    if (F > 0) {
-        const int ws = F >> 5, bs = F & 31;
-        for (int q = kLimbs - 1; q >= 0; --q) {
-            const int src = q - ws;
-            uint32_t hi = (src >= 0) ? N[src] : 0u;
-            uint32_t lo = (src - 1 >= 0) ? N[src - 1] : 0u;
-            N[q] = bs ? ((hi << bs) | (lo >> (32 - bs))) : hi;
-        }
-    }
-    // Q = N / cnt, remainder r  (cnt < 2^32)
-    uint32_t Q[kLimbs];
-    unsigned long long r = 0ull;
-    for (int q = kLimbs - 1; q >= 0; --q) {
-        const unsigned long long cur = (r << 32) | N[q];
-        Q[q] = (uint32_t)(cur / cnt);
-        r = cur % cnt;
-    }
-    int L = 0;
-    for (int q = kLimbs - 1; q >= 0; --q)
-        if (Q[q]) { L = 32 * q + (32 - __clz(Q[q])); break; }
-    int shift = L - 24;
-    if (shift < F) shift = F;  // subnormal result: LSB weight 2^-149
-    auto bit = [&](int i) -> uint32_t { return (i < 0) ? 0u : ((Q[i >> 5] >> (i & 31)) & 1u); };
-    uint32_t kept = 0u;
-    for (int i = 24; i >= 0; --i) kept = (kept << 1) | bit(shift + i);
-    const uint32_t round_bit = bit(shift - 1);
-    bool sticky = r != 0ull;
-    for (int i = 0; i < shift - 1 && !sticky; ++i) sticky = bit(i) != 0u;
-    if (round_bit && (sticky || (kept & 1u))) kept += 1u;
-    int ex = shift - 149 - F;  // value = kept * 2^ex
-    if (kept == (1u << 24)) { kept >>= 1; ex += 1; }
-    if (kept == 0u) return 0.0f;
-    uint32_t bits;
-    if (kept >= (1u << 23)) bits = ((uint32_t)(ex + 150) << 23) | (kept - (1u << 23));
-    else bits = kept;  // subnormal: ex == -149
-    return __uint_as_float(bits);
-}
+// Exact mean -> fp32, nearest even.
+// N = sum_eb bucket[eb] * 2^(eb-1) is the sum of the magnitudes in units of
+// 2^-149 (< 2^311), the mean is N / cnt * 2^-149 with cnt < 2^32.
+// Let T = bitlen(N), E = max(0, T - 64), Ntop = N >> E (exactly N when
+// N < 2^64, which covers every subnormal result).  With Q1 = Ntop / cnt and
+// r1 = Ntop % cnt,  N / cnt = Q1 * 2^E + d  with 0 <= d < 2^E and d = 0 iff
+// r1 == 0 and the low E bits of N are zero.  Q1 has >= 32 significant bits
+// when E > 0, so Q1 plus that sticky bit decide the rounding exactly.
+constexpr int kLimbs = 10;  // 320 bits
 
 __global__ void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k, float* __restrict__ scales)
 {
-    const int axis = threadIdx.x;
-    if (axis >= 2) return;
+    __shared__ unsigned long long s_part[2][16];
+    const int axis = threadIdx.x >> 5;  // 2 x 32 threads
+    const int L = threadIdx.x & 31;
     const unsigned long long* g = ws + (int64_t)k * kStageWords;
-    scales[2 * k + axis] = exact_mean_f32(g + 256 * axis, g[kBuckets + axis]);
+    const unsigned long long* buck = g + 256 * axis;
+    // thread L sums the 32-bit slices of every bucket that land in limb L
+    if (L < kLimbs) {
+        unsigned long long acc = 0ull;
+        for (int eb = 1; eb < 256; ++eb) {
+            const unsigned long long v = buck[eb];
+            if (!v) continue;
+            const int sh = eb - 1 - 32 * L;  // v * 2^(eb-1) seen from bit 32L
+            uint32_t piece;
+            if (sh >= 32 || sh <= -64) piece = 0u;
+            else if (sh >= 0) piece = (uint32_t)(v << sh);
+            else piece = (uint32_t)(v >> (-sh));
+            acc += piece;
+        }
+        s_part[axis][L] = acc;
+    }
+    __syncthreads();
+    if (L != 0) return;
+    const unsigned long long cnt = g[kBuckets + axis];
+    float result = 0.0f;
+    if (cnt != 0ull) {
+        uint32_t N[kLimbs];
+        unsigned long long carry = 0ull;
+#pragma unroll
+        for (int q = 0; q < kLimbs; ++q) {
+            const unsigned long long t = s_part[axis][q] + carry;
+            N[q] = (uint32_t)t;
+            carry = t >> 32;
+        }
+        int T = 0;
+#pragma unroll
+        for (int q = 0; q < kLimbs; ++q)
+            if (N[q]) T = 32 * q + (32 - __clz(N[q]));
+        if (T > 0) {
+            const int E = T > 64 ? T - 64 : 0;
+            // Ntop = N >> E and the sticky bit of the shifted-out part
+            unsigned long long top = 0ull;
+            bool low = false;
+#pragma unroll
+            for (int q = 0; q < kLimbs; ++q) {
+                const int pos = 32 * q - E;  // bit position of limb q inside Ntop
+                const unsigned long long v = N[q];
+                if (pos >= 64 || pos <= -32) {
+                    if (pos <= -32 && v) low = true;
+                } else if (pos >= 0) {
+                    top |= v << pos;
+                } else {
+                    top |= v >> (-pos);
+                    if (v & ((1ull << (-pos)) - 1ull)) low = true;
+                }
+            }
+            const unsigned long long Q1 = top / cnt, r1 = top % cnt;
+            const bool sticky0 = low || r1 != 0ull;
+            // value = (Q1 + frac) * 2^(E - 149);  keep 24 bits (or the subnormal LSB 2^-149)
+            const int L1 = 64 - __clzll(Q1);
+            int shift = L1 - 24;
+            if (shift < -E) shift = -E;  // LSB weight may not fall below 2^-149
+            // shift >= 0 always: E > 0 gives L1 >= 32, E == 0 clamps shift at 0
+            unsigned long long kept;
+            bool rbit, sticky;
+            if (shift > 0) {
+                kept = Q1 >> shift;
+                rbit = (Q1 >> (shift - 1)) & 1ull;
+                sticky = sticky0 || (shift > 1 && (Q1 & ((1ull << (shift - 1)) - 1ull)));
+            } else {
+                // E == 0: Q1 = floor(N / cnt) exactly; the discarded part is r1 / cnt
+                kept = Q1;
+                rbit = 2ull * r1 >= cnt;
+                sticky = 2ull * r1 > cnt;
+            }
+            if (rbit && (sticky || (kept & 1ull))) kept += 1ull;
+            int ex = shift + E - 149;  // value = kept * 2^ex
+            if (kept == (1ull << 24)) { kept >>= 1; ex += 1; }
+            uint32_t bits = 0u;
+            if (kept >= (1ull << 23)) bits = ((uint32_t)(ex + 150) << 23) | (uint32_t)(kept - (1ull << 23));
+            else bits = (uint32_t)kept;  // subnormal: ex == -149
+            result = __uint_as_float(bits);
+        }
+    }
+    scales[2 * k + axis] = result;
 }
 
 __global__ __launch_bounds__(kThreads) void k_pq_resid(const float* __restrict__ w_re,

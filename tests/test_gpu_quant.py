@@ -95,3 +95,30 @@ def test_pack_ignores_high_bits():
     packed = pack_on_gpu(dev(noisy), 1, 4, 64)
     torch().cuda.synchronize()
     assert np.array_equal(host(packed, np.uint32), oracle.pack(c, oracle.TILED64))
+
+
+def test_phasequant_scale_rounding_fixtures():
+    """The hand-worked mean-rounding cases (ties to even, subnormal means) as
+    real-axis weights: s_re must be the fixture value, s_im 0."""
+    from tests._golden import hex_to_f32, rows
+    for line in rows("abs_mean_rounding.txt"):
+        want, vals = line.split(";")
+        re = np.array([hex_to_f32(h) for h in vals.split()], np.float32)
+        im = np.zeros_like(re)
+        codes, scales, _, _ = phasequant_on_gpu(dev(re), dev(im), re.size, 1, want_resid=False)
+        torch().cuda.synchronize()
+        got = host(scales).view(np.uint32)
+        assert got[0] == hex_to_f32(want.strip()).view(np.uint32), line
+        assert got[1] == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_phasequant_wide_dynamic_range(seed):
+    """Magnitudes spread over the whole fp32 range in one tensor."""
+    g = synth.rng(500 + seed)
+    k = 20000
+    e = g.integers(-149, 120, size=k).astype(np.float64)
+    re = ((g.random(k) + 0.5) * np.exp2(e) * np.where(g.random(k) < 0.5, -1, 1)).astype(np.float32)
+    e2 = g.integers(-149, 120, size=k).astype(np.float64)
+    im = ((g.random(k) + 0.5) * np.exp2(e2) * np.where(g.random(k) < 0.5, -1, 1)).astype(np.float32)
+    _check_pq(re, im, 2)
