@@ -2,7 +2,7 @@
 //
 // The prefill layer is the decode layer applied to M token rows at once
 // [Fairy2i article §4.2]; at M in the thousands it is a dense contraction.
-#include "fairy_internal.h"
+#include "fairy_gemv_impl.h"
 
 namespace fairy {
 
@@ -20,7 +20,13 @@ hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, 
                         void* workspace, hipStream_t s)
 {
     (void)workspace;
-    if (algo == FAIRY_ALGO_MFMA) return hipErrorNotSupported;
+    const bool mfma_ok = xdtype == FAIRY_BF16 || xdtype == FAIRY_I8;
+    const bool use_mfma = (algo == FAIRY_ALGO_MFMA) || (algo == FAIRY_ALGO_AUTO && mfma_ok && M >= 32);
+    if (use_mfma) {
+        if (!mfma_ok) return hipErrorNotSupported;
+        const gemv::GemvArgs a = gemv::make_args(L, x_re, x_im, M, ldx, y_re, y_im, ldy, acc);
+        return launch_cgemm_mfma(a, xdtype, s);
+    }
     // VALU path: the decode kernel streams the token rows through LDS in
     // chunks, re-reading the (L2-resident) codes per chunk.
     return launch_cgemv(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, s);

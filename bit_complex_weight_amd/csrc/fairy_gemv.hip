@@ -26,10 +26,11 @@ int pick_bch(int xdtype, int B, int m64)
 
 }  // namespace gemv
 
-hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype, int64_t batch,
-                        int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc, hipStream_t s)
+namespace gemv {
+GemvArgs make_args(const LayerArgs& L, const void* x_re, const void* x_im, int64_t batch, int64_t ldx,
+                   float* y_re, float* y_im, int64_t ldy, int32_t* acc)
 {
-    gemv::GemvArgs a;
+    GemvArgs a;
     a.packed = L.packed;
     a.scales = L.scales;
     a.x_re = x_re;
@@ -46,6 +47,14 @@ hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, 
     a.S = L.stages;
     a.P = L.planes;
     a.B = (int32_t)batch;
+    return a;
+}
+}  // namespace gemv
+
+hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype, int64_t batch,
+                        int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc, hipStream_t s)
+{
+    const gemv::GemvArgs a = gemv::make_args(L, x_re, x_im, batch, ldx, y_re, y_im, ldy, acc);
     if (gemv::kScaleBytes + (size_t)gemv::x_bytes_per_col(xdtype, a.m64) > 64 * 1024) return hipErrorInvalidValue;
     switch (xdtype) {
     case FAIRY_BF16: return gemv::launch_bf16(a, s);

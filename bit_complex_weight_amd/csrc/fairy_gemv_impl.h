@@ -422,5 +422,11 @@ hipError_t launch_bf16(const GemvArgs& a, hipStream_t s);
 hipError_t launch_f32(const GemvArgs& a, hipStream_t s);
 hipError_t launch_i8(const GemvArgs& a, hipStream_t s);
 
+GemvArgs make_args(const LayerArgs& L, const void* x_re, const void* x_im, int64_t batch, int64_t ldx,
+                   float* y_re, float* y_im, int64_t ldy, int32_t* acc);
+
 }  // namespace gemv
+
+// matrix-core prefill (fairy_gemm_mfma.hip); a.B is the token count
+hipError_t launch_cgemm_mfma(const gemv::GemvArgs& a, int32_t xdtype, hipStream_t s);
 }  // namespace fairy

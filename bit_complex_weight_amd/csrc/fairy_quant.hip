@@ -119,19 +119,28 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t count)
 // Stage k: recompute R_k from W with the scales of stages < k (already on
 // the device), write code_k, and add |R_k| on the code's axis into the
 // stage's exponent buckets (block-local LDS buckets, flushed once per block).
+// Stage k: recompute R_k from W with the scales of stages < k (already on
+// the device), write code_k, and add |R_k| on the code's axis into the
+// stage's exponent buckets.  Buckets live in LDS in kCopies interleaved copies
+// (lane % kCopies picks one) so lanes of a wave hitting the same exponent
+// rarely collide on one address; the copies are summed when the block flushes
+// its nonzero buckets to the workspace with integer atomics.
+constexpr int kCopies = 8;
+
 __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__ w_re,
                                                        const float* __restrict__ w_im, int64_t count,
                                                        int32_t k, const float* __restrict__ scales,
                                                        uint8_t* __restrict__ codes,
                                                        unsigned long long* __restrict__ ws)
 {
-    __shared__ unsigned long long s_buck[kBuckets];
+    __shared__ unsigned long long s_buck[kBuckets * kCopies];
     __shared__ unsigned long long s_cnt[2];
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) s_buck[t] = 0ull;
+    for (int t = threadIdx.x; t < kBuckets * kCopies; t += blockDim.x) s_buck[t] = 0ull;
     if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0ull;
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
+    const int copy = threadIdx.x % kCopies;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < count; base += stride) {
         const int64_t i = base + threadIdx.x;
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
             const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
             const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
             const uint32_t sig = ex ? (man | 0x800000u) : man;
-            if (sig) atomicAdd(&s_buck[axis * 256u + (ex ? ex : 1u)], (unsigned long long)sig);
+            if (sig) atomicAdd(&s_buck[(axis * 256u + (ex ? ex : 1u)) * kCopies + copy], (unsigned long long)sig);
         }
         // counts per axis: one ballot per wave instead of per-element atomics
         const unsigned long long im_mask = __ballot(valid && axis == 1u);
@@ -160,8 +169,12 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
     }
     __syncthreads();
     unsigned long long* g = ws + (int64_t)k * kStageWords;
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x)
-        if (s_buck[t]) atomicAdd(&g[t], s_buck[t]);
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) {
+        unsigned long long v = 0ull;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) v += s_buck[t * kCopies + c];
+        if (v) atomicAdd(&g[t], v);
+    }
     if (threadIdx.x < 2 && s_cnt[threadIdx.x]) atomicAdd(&g[kBuckets + threadIdx.x], s_cnt[threadIdx.x]);
 }
 
@@ -178,10 +191,13 @@ constexpr int kLimbs = 10;  // 320 bits
 __global__ void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k, float* __restrict__ scales)
 {
     __shared__ unsigned long long s_part[2][16];
+    __shared__ unsigned long long s_b[kBuckets];
     const int axis = threadIdx.x >> 5;  // 2 x 32 threads
     const int L = threadIdx.x & 31;
     const unsigned long long* g = ws + (int64_t)k * kStageWords;
-    const unsigned long long* buck = g + 256 * axis;
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) s_b[t] = g[t];  // one parallel read
+    __syncthreads();
+    const unsigned long long* buck = s_b + 256 * axis;
     // thread L sums the 32-bit slices of every bucket that land in limb L
     if (L < kLimbs) {
         unsigned long long acc = 0ull;
