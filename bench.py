@@ -9,15 +9,17 @@ activations (batch 1 by default, N(0,1), seed 201).
 
 Each timed step reads a different copy of the packed weights from a pool of
 >= 512 MiB, so the codes really stream from HBM (no L2 / Infinity-Cache
-reuse).  `value` is packed-weight GB/s over the timed steps.
+reuse).  The K steps are captured once as a HIP graph and replayed, so the
+Python binding's launch cost is not measured; `value` is packed-weight GB/s
+over the timed steps.
 
-Also reported: the roofline of the GEMV kernel (HBM-bound, achieved bytes
+Also reported: the roofline of the GEMV kernel (HBM-bound, algorithmic bytes
 per launch over the average launch time from HIP events on the launch
 stream), the CPU oracle on a bounded sample of the same workload, and the
-other rows of the path (conversion, PhaseQuant, pack, larger batches, the
-prefill GEMM) timed the same way.
+other rows of the path (conversion, PhaseQuant, pack, the MLP shapes, larger
+batches, the prefill GEMM on the matrix cores and on the VALUs).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B] [--sweep]
 """
 import argparse
 import json
@@ -32,11 +34,126 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0}   # dense
 POOL_BYTES = 512 << 20
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Bench:
+    def __init__(self):
+        import torch
+        from bit_complex_weight_amd import fairy as F
+        from bit_complex_weight_amd import synth
+        self.torch, self.F, self.synth = torch, F, synth
+        torch.cuda.set_device(0)
+        self.stream = torch.cuda.current_stream()
+
+    def dev(self, a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return self.torch.from_numpy(a).cuda()
+
+    def ev_time(self, fn, iters):
+        """Average ms per call of fn(i) over iters back-to-back calls (HIP events
+        on the launch stream)."""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for i in range(iters):
+            fn(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    def graph_time(self, fn, steps):
+        """Capture `steps` calls fn(i) as one HIP graph, replay once untimed,
+        then time one replay; returns (ms per call, graph)."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ms = self.ev_time(lambda i: g.replay(), 1) / steps
+        return ms, g
+
+    def widely_linear_layer(self, rows, cols, S, seed):
+        """Real [rows][cols] N(0, 0.02^2) -> U, W -> S stages -> TILED64, all on the GPU."""
+        torch, F = self.torch, self.F
+        n, m = rows // 2, cols // 2
+        P = 2 * S
+        R = self.dev(self.synth.real_layer(rows, cols, seed))
+        planes = [torch.empty((n, m), dtype=torch.float32, device="cuda") for _ in range(4)]
+        F.fairy_real_to_complex(R, n, m, *planes)
+        count = n * m
+        codes = torch.empty((P, n, m), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((P, 2), dtype=torch.float32, device="cuda")
+        wsb = F.fairy_phasequant_workspace_bytes(count, S)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        F.fairy_phasequant(planes[0], planes[1], count, S, codes[0], scales[0], None, None, ws, wsb)
+        F.fairy_phasequant(planes[2], planes[3], count, S, codes[S], scales[S], None, None, ws, wsb)
+        nw = F.fairy_packed_words(n, m, P, F.FAIRY_LAYOUT_TILED64)
+        packed = torch.empty(nw, dtype=torch.int32, device="cuda")
+        F.fairy_pack(codes, P, n, m, F.FAIRY_LAYOUT_TILED64, packed)
+        torch.cuda.synchronize()
+        return dict(R=R, planes=planes, codes=codes, scales=scales, ws=ws, wsb=wsb, packed=packed,
+                    n=n, m=m, S=S, P=P, count=count, packed_bytes=nw * 4)
+
+    def pool(self, L, has_conj=1):
+        ncopy = max(2, math.ceil(POOL_BYTES / L["packed_bytes"]))
+        copies = [L["packed"].clone() for _ in range(ncopy)]
+        descs = [self.F.make_clinear(L["n"], L["m"], L["S"], has_conj, p, L["scales"]) for p in copies]
+        return copies, descs
+
+    def gemv_rate(self, L, descs, B, xdtype, steps=200, seed=202):
+        torch, F = self.torch, self.F
+        n, m = L["n"], L["m"]
+        if xdtype == F.FAIRY_I8:
+            xr, xi = self.synth.int8_uniform((B, m), seed)
+        else:
+            xr, xi = self.synth.bf16_gaussian((B, m), seed)
+        xr, xi = self.dev(xr), self.dev(xi)
+        yr = torch.empty((B, n), dtype=torch.float32, device="cuda")
+        yi = torch.empty((B, n), dtype=torch.float32, device="cuda")
+        f = lambda i: F.fairy_cgemv(descs[i % len(descs)], xr, xi, xdtype, B, m, yr, yi, n)
+        f(0)
+        ms, _ = self.graph_time(f, steps)
+        return ms
+
+    def gemm_rate(self, L, desc, M, xdtype, algo, iters=5, seed=204):
+        torch, F = self.torch, self.F
+        n, m = L["n"], L["m"]
+        if xdtype == F.FAIRY_I8:
+            xr, xi = self.synth.int8_uniform((M, m), seed)
+        else:
+            xr, xi = self.synth.bf16_gaussian((M, m), seed)
+        xr, xi = self.dev(xr), self.dev(xi)
+        yr = torch.empty((M, n), dtype=torch.float32, device="cuda")
+        yi = torch.empty((M, n), dtype=torch.float32, device="cuda")
+        f = lambda i: F.fairy_cgemm(desc, xr, xi, xdtype, M, m, yr, yi, n, None, algo)
+        f(0)
+        return self.ev_time(f, iters)
+
+
+def gemm_entry(ms, P, n, m, M, peak=None):
+    alg = 2.0 * P * n * m * M            # additions of the multiplication-free form
+    mfma_ops = 8.0 * P * n * m * M       # 2 x MACs on the ternary planes (4 MACs per code per token)
+    out = {"ms": ms, "alg_TOPS": alg / (ms * 1e-3) / 1e12}
+    if peak:
+        t = mfma_ops / (ms * 1e-3) / 1e12
+        out.update({"mfma_TOPS": t, "mfma_peak_TOPS": peak, "mfma_frac": t / peak})
+    return out
 
 
 def main():
@@ -46,8 +163,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings")
+    ap.add_argument("--no-rows", action="store_true", help="skip the other rows of the path")
+    ap.add_argument("--sweep", action="store_true", help="also run the full-layer sweep (slow)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib", action="store_true",
+                    help="only measure the ceilings: a plain 256 MiB copy (the byte-counter calibration "
+                         "kernel), 4 MiB and 32 MiB copy launches and tiny launches in HIP graphs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -55,90 +176,44 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    from bit_complex_weight_amd import fairy as F
-    from bit_complex_weight_amd import synth
+    bn = Bench()
+    torch, F, synth = bn.torch, bn.F, bn.synth
+    if args.calib:
+        print(json.dumps(calibrate(bn)), flush=True)
+        return
 
-    torch.cuda.set_device(0)
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    stream = torch.cuda.current_stream()
-
-    def ev_time(fn, iters):
-        """Average ms per call of fn(i) over iters back-to-back calls (HIP events)."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(iters):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
-
-    # ---- build the layer on the GPU: conversion -> PhaseQuant -> pack -------
-    rows, cols, S = 4096, 4096, 2
-    n, m = rows // 2, cols // 2
-    P = 2 * S
-    log(f"building widely-linear {rows}x{cols} -> {n}x{m}, S={S}")
-    R = synth.real_layer(rows, cols, seed=200)
-    R_d = dev(R)
-    planes = [torch.empty((n, m), dtype=torch.float32, device="cuda") for _ in range(4)]
-    F.fairy_real_to_complex(R_d, n, m, *planes)
-    count = n * m
-    codes = torch.empty((P, n, m), dtype=torch.uint8, device="cuda")
-    scales = torch.empty((P, 2), dtype=torch.float32, device="cuda")
-    wsb = F.fairy_phasequant_workspace_bytes(count, S)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    F.fairy_phasequant(planes[0], planes[1], count, S, codes[0], scales[0], None, None, ws, wsb)
-    F.fairy_phasequant(planes[2], planes[3], count, S, codes[S], scales[S], None, None, ws, wsb)
-    nw = F.fairy_packed_words(n, m, P, F.FAIRY_LAYOUT_TILED64)
-    packed = torch.empty(nw, dtype=torch.int32, device="cuda")
-    F.fairy_pack(codes, P, n, m, F.FAIRY_LAYOUT_TILED64, packed)
-    torch.cuda.synchronize()
-    packed_bytes = nw * 4
-
-    ncopy = max(2, math.ceil(POOL_BYTES / packed_bytes))
-    pool = [packed.clone() for _ in range(ncopy)]
-    descs = [F.make_clinear(n, m, S, 1, p, scales) for p in pool]
+    # ---- the metric's workload ------------------------------------------------------
+    log("building widely-linear 4096x4096 -> 2048x2048, S=2")
+    L = bn.widely_linear_layer(4096, 4096, 2, seed=200)
+    n, m, S, P, packed_bytes = L["n"], L["m"], L["S"], L["P"], L["packed_bytes"]
+    copies, descs = bn.pool(L)
+    ncopy = len(copies)
 
     B = args.batch
     rb, ib = synth.bf16_gaussian((B, m), seed=201)
-    x_re, x_im = dev(rb.view(np.int16)), dev(ib.view(np.int16))
+    x_re, x_im = bn.dev(rb), bn.dev(ib)
     y_re = torch.empty((B, n), dtype=torch.float32, device="cuda")
     y_im = torch.empty((B, n), dtype=torch.float32, device="cuda")
 
     def gemv(i):
         F.fairy_cgemv(descs[i % ncopy], x_re, x_im, F.FAIRY_BF16, B, m, y_re, y_im, n)
 
-    # ---- timed region: the K steps are captured once as a HIP graph (K GEMV
-    # launches, each on its own weight copy) and replayed, so the host-side
-    # launch cost of the Python binding is not part of the measurement.
     for i in range(args.warmup):
         gemv(i)
     torch.cuda.synchronize()
     eager_y = (y_re.clone(), y_im.clone())
-    eager_ms = ev_time(gemv, min(args.steps, 200))
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(args.steps):
-                gemv(i)
-    torch.cuda.synchronize()
+    eager_ms = bn.ev_time(gemv, min(args.steps, 200))
     y_re.zero_(); y_im.zero_()
-    graph.replay()                                   # untimed warm replay
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms, graph = bn.graph_time(gemv, args.steps)
+    wall = time.perf_counter() - t0
     if not (torch.equal(y_re, eager_y[0]) and torch.equal(y_im, eager_y[1])):
         raise SystemExit("graph replay output differs from the eager GEMV output")
-    t0 = time.perf_counter()
-    ms = ev_time(lambda i: graph.replay(), 1) / args.steps
-    wall = time.perf_counter() - t0
     gbs = packed_bytes / (ms * 1e-3) / 1e9
     alg_bytes = packed_bytes + B * m * 2 * 2 + B * n * 2 * 4
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     log(f"GEMV B={B}: graph {ms * 1e3:.2f} us/launch ({gbs:.0f} GB/s packed), eager {eager_ms * 1e3:.2f} us/call, "
-        f"wall {wall:.4f}s for {args.steps}")
+        f"capture+replay wall {wall:.3f}s for {args.steps}")
 
     result = {
         "metric": "GB/s & % HBM peak, 2-bit complex GEMV at LLaMA-2-7B shapes; prefill TOPS",
@@ -160,6 +235,7 @@ def main():
             "n": n, "m": m, "stages": S, "planes": P, "batch": B,
             "packed_bytes": packed_bytes, "weight_pool_bytes": packed_bytes * ncopy,
             "complex_weights_per_s": P * n * m / (ms * 1e-3),
+            "hbm_frac_packed": round(gbs / HBM_PEAK_GBS, 4),
         },
         "roofline": {
             "bound": "hbm",
@@ -168,57 +244,72 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "k_cgemv_units<bf16>",
-            "eager_ms_per_call": eager_ms,
+            "kernel": "k_cgemv_units<bf16,64,1,2>",
             "alg_bytes_per_launch": alg_bytes,
+            "eager_ms_per_call": eager_ms,
         },
     }
 
-    # ---- other rows of the path --------------------------------------------------
+    # ---- other rows of the path ---------------------------------------------------------
     if not args.no_rows:
         rows_out = {}
-        it = 20
-        ms_c = ev_time(lambda i: F.fairy_real_to_complex(R_d, n, m, *planes), it)
-        rows_out["real_to_complex"] = {"ms": ms_c, "GB/s": (4 * rows * cols * 2) / (ms_c * 1e-3) / 1e9}
-        ms_q = ev_time(lambda i: F.fairy_phasequant(planes[0], planes[1], count, S, codes[0], scales[0], None,
-                                                    None, ws, wsb), it)
-        rows_out["phasequant_S2_per_matrix"] = {"ms": ms_q, "unique_GB/s": (count * 8) / (ms_q * 1e-3) / 1e9}
-        ms_p = ev_time(lambda i: F.fairy_pack(codes, P, n, m, F.FAIRY_LAYOUT_TILED64, packed), it)
-        rows_out["pack"] = {"ms": ms_p, "GB/s": (P * count * 1.25) / (ms_p * 1e-3) / 1e9}
+        R, planes, codes, scales, ws, wsb = L["R"], L["planes"], L["codes"], L["scales"], L["ws"], L["wsb"]
+        count = L["count"]
+        ms_c = bn.ev_time(lambda i: F.fairy_real_to_complex(R, n, m, *planes), 20)
+        rows_out["real_to_complex_4096x4096"] = {"ms": ms_c, "GB/s": (4 * 4 * n * m * 2) / (ms_c * 1e-3) / 1e9}
+        ms_q = bn.ev_time(lambda i: F.fairy_phasequant(planes[0], planes[1], count, S, codes[0], scales[0], None,
+                                                       None, ws, wsb), 20)
+        rows_out["phasequant_S2_2048x2048"] = {"ms": ms_q, "unique_GB/s": (count * 8) / (ms_q * 1e-3) / 1e9}
+        ms_p = bn.ev_time(lambda i: F.fairy_pack(codes, P, n, m, F.FAIRY_LAYOUT_TILED64, L["packed"]), 20)
+        rows_out["pack_P4_2048x2048"] = {"ms": ms_p, "GB/s": (P * count * 1.25) / (ms_p * 1e-3) / 1e9}
         for bb in (4, 16, 64):
-            rbb, ibb = synth.bf16_gaussian((bb, m), seed=202)
-            xr2, xi2 = dev(rbb.view(np.int16)), dev(ibb.view(np.int16))
-            yr2 = torch.empty((bb, n), dtype=torch.float32, device="cuda")
-            yi2 = torch.empty((bb, n), dtype=torch.float32, device="cuda")
-            f = lambda i: F.fairy_cgemv(descs[i % ncopy], xr2, xi2, F.FAIRY_BF16, bb, m, yr2, yi2, n)
-            f(0)
-            msb = ev_time(f, 50)
-            rows_out[f"gemv_bf16_B{bb}"] = {"ms": msb, "packed_GB/s": packed_bytes / (msb * 1e-3) / 1e9,
-                                           "alg_Tadds/s": 2 * P * n * m * bb / (msb * 1e-3) / 1e12}
-        xi8r, xi8i = synth.int8_uniform((1, m), seed=203)
-        xr8, xi8 = dev(xi8r), dev(xi8i)
-        f = lambda i: F.fairy_cgemv(descs[i % ncopy], xr8, xi8, F.FAIRY_I8, 1, m, y_re[:1], y_im[:1], n)
-        f(0)
-        ms8 = ev_time(f, 200)
-        rows_out["gemv_i8_B1"] = {"ms": ms8, "packed_GB/s": packed_bytes / (ms8 * 1e-3) / 1e9}
-        Mg = 2048
-        rg, ig = synth.bf16_gaussian((Mg, m), seed=204)
-        xgr, xgi = dev(rg.view(np.int16)), dev(ig.view(np.int16))
-        ygr = torch.empty((Mg, n), dtype=torch.float32, device="cuda")
-        ygi = torch.empty((Mg, n), dtype=torch.float32, device="cuda")
-        fg = lambda i: F.fairy_cgemm(descs[0], xgr, xgi, F.FAIRY_BF16, Mg, m, ygr, ygi, n, None,
-                                     F.FAIRY_ALGO_VALU)
-        fg(0)
-        msg = ev_time(fg, 3)
-        rows_out["gemm_bf16_valu_M2048"] = {"ms": msg, "alg_TOPS": 2 * P * n * m * Mg / (msg * 1e-3) / 1e12}
+            msb = bn.gemv_rate(L, descs, bb, F.FAIRY_BF16, steps=100)
+            rows_out[f"gemv_2048x2048_bf16_B{bb}"] = {
+                "ms": msb, "packed_GB/s": packed_bytes / (msb * 1e-3) / 1e9,
+                "alg_Tadds/s": 2 * P * n * m * bb / (msb * 1e-3) / 1e12}
+        ms8 = bn.gemv_rate(L, descs, 1, F.FAIRY_I8, steps=200)
+        rows_out["gemv_2048x2048_i8_B1"] = {"ms": ms8, "packed_GB/s": packed_bytes / (ms8 * 1e-3) / 1e9}
+        del copies, descs
+        torch.cuda.empty_cache()
+        # MLP shapes (gate/up: 11008x4096, down: 4096x11008)
+        for name, (rr, cc, sd) in {"gate_up_5504x2048": (11008, 4096, 300),
+                                   "down_2048x5504": (4096, 11008, 302)}.items():
+            L2 = bn.widely_linear_layer(rr, cc, 2, sd)
+            c2, d2 = bn.pool(L2)
+            for bb in (1, 8):
+                msm = bn.gemv_rate(L2, d2, bb, F.FAIRY_BF16, steps=200)
+                rows_out[f"gemv_{name}_bf16_B{bb}"] = {
+                    "ms": msm, "packed_GB/s": L2["packed_bytes"] / (msm * 1e-3) / 1e9}
+            del c2, d2
+            if name.startswith("gate"):
+                # prefill GEMM, M = 2048 tokens, on the 5504-row layer
+                d1 = F.make_clinear(L2["n"], L2["m"], 2, 1, L2["packed"], L2["scales"])
+                msg = bn.gemm_rate(L2, d1, 2048, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA)
+                rows_out["gemm_5504x2048_M2048_bf16_mfma"] = gemm_entry(msg, 4, L2["n"], L2["m"], 2048,
+                                                                        MFMA_PEAK_TFLOPS["bf16"])
+                msg = bn.gemm_rate(L2, d1, 2048, F.FAIRY_I8, F.FAIRY_ALGO_MFMA)
+                rows_out["gemm_5504x2048_M2048_i8_mfma"] = gemm_entry(msg, 4, L2["n"], L2["m"], 2048,
+                                                                      MFMA_PEAK_TFLOPS["i8"])
+            del L2
+            torch.cuda.empty_cache()
+        d0 = F.make_clinear(n, m, S, 1, L["packed"], L["scales"])
+        for dt, dn in ((F.FAIRY_BF16, "bf16"), (F.FAIRY_I8, "i8")):
+            msg = bn.gemm_rate(L, d0, 2048, dt, F.FAIRY_ALGO_MFMA)
+            rows_out[f"gemm_2048x2048_M2048_{dn}_mfma"] = gemm_entry(msg, P, n, m, 2048, MFMA_PEAK_TFLOPS[dn])
+            msg = bn.gemm_rate(L, d0, 2048, dt, F.FAIRY_ALGO_VALU, iters=2)
+            rows_out[f"gemm_2048x2048_M2048_{dn}_valu"] = gemm_entry(msg, P, n, m, 2048)
         result["rows"] = rows_out
         log(json.dumps(rows_out))
 
-    # ---- CPU oracle baseline (bounded sample of the same workload) ---------------
+    if args.sweep:
+        result["sweep"] = full_layer_sweep(bn)
+
+    # ---- CPU oracle baseline (bounded sample of the same workload) ---------------------
     if not args.no_cpu:
         import oracle
         cores = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1))
-        ur, ui, wr, wi = oracle.real_to_complex(R, n, m, f32=True)
+        Rh = synth.real_layer(4096, 4096, 200)
+        ur, ui, wr, wi = oracle.real_to_complex(Rh, n, m, f32=True)
         cu, su, _, _ = oracle.phasequant(ur, ui, S, want_resid=False)
         cw, sw, _, _ = oracle.phasequant(wr, wi, S, want_resid=False)
         oc = np.concatenate([cu, cw]); osc = np.concatenate([su, sw])
@@ -228,7 +319,7 @@ def main():
             oracle.cgemv_dense(oc, osc, S, True, xr, xi)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or reps >= 1000:
+            if el >= args.cpu_seconds or reps >= 2000:
                 break
         result["cpu_baseline"] = {
             "value": round(packed_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
@@ -238,6 +329,86 @@ def main():
         }
 
     print(json.dumps(result), flush=True)
+
+
+def calibrate(bn):
+    """Ceilings of the part, with plain copies: one of known size (256 MiB in,
+    256 MiB out; its FETCH_SIZE / WRITE_SIZE calibrate the byte counters),
+    copies moving 4 MiB and 32 MiB per launch over a 1 GiB pool, and tiny
+    launches, each of the latter captured as a HIP graph."""
+    torch = bn.torch
+    out = {}
+    src = torch.randint(0, 1 << 30, (64 << 20,), dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = bn.ev_time(lambda i: dst.copy_(src), 10)
+    out["copy_256MiB"] = {"ms": ms, "bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                          "GB/s_read+write": 2 * src.numel() * 4 / (ms * 1e-3) / 1e9}
+    pool = torch.ones((1 << 28,), dtype=torch.int32, device="cuda")     # 1 GiB
+    for mib in (4, 32):
+        # one launch moves `mib` MiB: a copy of mib/2 MiB between two distinct
+        # slices of the pool (half read, half written)
+        n = (mib << 20) // 8
+        k = pool.numel() // (2 * n)
+        f = lambda i: pool[(2 * (i % k) + 1) * n:(2 * (i % k) + 2) * n].copy_(pool[2 * (i % k) * n:(2 * (i % k) + 1) * n])
+        f(0)
+        ms, _ = bn.graph_time(f, 128)
+        out[f"copy_{mib}MiB_traffic_per_launch"] = {"us": ms * 1e3, "GB/s": (mib << 20) / (ms * 1e-3) / 1e9}
+    e = torch.empty((1,), dtype=torch.int32, device="cuda")
+    ms, _ = bn.graph_time(lambda i: e.zero_(), 256)
+    out["tiny_launch_us"] = ms * 1e3
+    return out
+
+
+def full_layer_sweep(bn):
+    """All seven projections of a LLaMA-2-7B-shaped layer in widely-linear form
+    with 1/2/3 residual stages and batch 1/4/16/64, plus a pure complex
+    (no conjugate branch) 2048x2048 and 8192x2048 layer set with PhaseQuant
+    timed on each.  Reports per-projection GEMV time and the layer total."""
+    F, torch, synth = bn.F, bn.torch, bn.synth
+    proj = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
+            "gate": (11008, 4096), "up": (11008, 4096), "down": (4096, 11008)}
+    out = {}
+    for S in (1, 2, 3):
+        layers = {name: bn.widely_linear_layer(rr, cc, S, 500 + 10 * S + i)
+                  for i, (name, (rr, cc)) in enumerate(proj.items())}
+        for B in (1, 4, 16, 64):
+            tot_ms, tot_bytes, per = 0.0, 0, {}
+            for name, L in layers.items():
+                copies, descs = bn.pool(L)
+                ms = bn.gemv_rate(L, descs, B, F.FAIRY_BF16, steps=100)
+                per[name] = ms
+                tot_ms += ms
+                tot_bytes += L["packed_bytes"]
+                del copies, descs
+                torch.cuda.empty_cache()
+            out[f"layer_S{S}_B{B}"] = {"ms_total": tot_ms, "packed_bytes": tot_bytes,
+                                        "packed_GB/s": tot_bytes / (tot_ms * 1e-3) / 1e9, "per_proj_ms": per}
+            log(f"sweep S={S} B={B}: {tot_ms * 1e3:.1f} us, {tot_bytes / (tot_ms * 1e-3) / 1e9:.0f} GB/s")
+        del layers
+        torch.cuda.empty_cache()
+    # pure complex layers (no conjugate branch): per-component sigma 0.02
+    for (n, m) in ((2048, 2048), (8192, 2048)):
+        for S in (1, 2):
+            re, im = synth.complex_gaussian((n, m), 0.02, 900 + n + S)
+            count = n * m
+            codes = torch.empty((S, n, m), dtype=torch.uint8, device="cuda")
+            scales = torch.empty((S, 2), dtype=torch.float32, device="cuda")
+            wsb = F.fairy_phasequant_workspace_bytes(count, S)
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            wre, wim = bn.dev(re), bn.dev(im)
+            ms_q = bn.ev_time(lambda i: F.fairy_phasequant(wre, wim, count, S, codes, scales, None, None, ws, wsb), 5)
+            nw = F.fairy_packed_words(n, m, S, F.FAIRY_LAYOUT_TILED64)
+            packed = torch.empty(nw, dtype=torch.int32, device="cuda")
+            F.fairy_pack(codes, S, n, m, F.FAIRY_LAYOUT_TILED64, packed)
+            L = dict(n=n, m=m, S=S, packed=packed, scales=scales, packed_bytes=nw * 4)
+            copies, descs = bn.pool(L, has_conj=0)
+            for B in (1, 16):
+                ms = bn.gemv_rate(L, descs, B, F.FAIRY_BF16, steps=100)
+                out[f"complex_{n}x{m}_S{S}_B{B}"] = {"ms": ms, "packed_GB/s": nw * 4 / (ms * 1e-3) / 1e9,
+                                                      "phasequant_ms": ms_q}
+            del copies, descs
+            torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
