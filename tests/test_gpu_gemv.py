@@ -182,6 +182,9 @@ GEMM_CASES = [
     (1, False, 64, 2048, 64),
     (2, True, 257, 512, 33),
     (4, True, 40, 128, 40),        # P = 8
+    (1, True, 130, 320, 65),       # P = 2
+    (3, False, 50, 192, 70),       # P = 3: a 2-plane pass, then a 1-plane pass adding into y
+    (7, False, 33, 64, 129),       # P = 7: 4 + 2 + 1 planes, three token blocks
 ]
 
 
