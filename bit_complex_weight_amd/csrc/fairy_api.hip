@@ -3,7 +3,7 @@
 // Every entry point validates its arguments on the host before touching the
 // HIP runtime; an invalid call launches nothing and writes nothing.  Errors
 // are reported as fairy_status codes, never by exceptions or printing.
-#include "fairy_internal.h"
+#include "fairy_gemv_impl.h"
 
 namespace {
 
@@ -25,10 +25,13 @@ bool valid_dtype(int32_t d) { return d == FAIRY_F32 || d == FAIRY_BF16 || d == F
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 
-// Largest m the v1 kernels stage in LDS (one batch column, 64 KiB).
+// Largest m whose staged activations (one batch column, re and im, 64-column
+// groups padded by 16 bytes, after the scale prefix) fit in 64 KiB of LDS:
+// 7680 (F32), 14528 (BF16), 26112 (I8).
 int64_t max_m_for(int32_t xdtype)
 {
-    return xdtype == FAIRY_F32 ? 8192 : xdtype == FAIRY_BF16 ? 16384 : 32768;
+    const int64_t groups = (64 * 1024 - fairy::gemv::kScaleBytes) / (2 * fairy::gemv::x_group_bytes(xdtype));
+    return 64 * groups;
 }
 
 // Checks shared by fairy_cgemv and fairy_cgemm.  Returns FAIRY_OK and fills

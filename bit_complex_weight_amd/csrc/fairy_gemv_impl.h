@@ -21,6 +21,13 @@
 // +-2 / 0 decoded values (fp32), and folds the plane's scales in once.  Row
 // partial sums are combined across the TROW lanes with DPP / ds_swizzle
 // butterflies: deterministic, no atomics.
+//
+// When the plane count P divides 64 and a row has at least 64 units, a wave
+// owns a row and lane l always sees plane l % P (units l + 64k): its scales
+// are per-lane constants, its four sums run over the whole row and are
+// scaled once before the cross-lane sum, and no index needs a division.
+// Those blocks have 8 waves (8 rows), so one staging of the activations
+// serves 8 rows.
 #pragma once
 
 #include "fairy_internal.h"
@@ -253,6 +260,86 @@ __global__ __launch_bounds__(kThreads) void k_cgemv_units(GemvArgs a)
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Float paths, plane count P dividing 64 and rows of >= 64 units: one row per
+// wave, lane l owns plane l % P and groups l/P + k*(64/P).
+// ---------------------------------------------------------------------------
+constexpr int kThreadsLp = 512;
+
+template <int XT, int P, int BCH>
+__global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
+{
+    static_assert(64 % P == 0, "plane count must divide the wave");
+    constexpr int GS = 64 / P;  // groups one step of the wave covers
+    constexpr int esize = (XT == FAIRY_BF16) ? 2 : 4;
+    constexpr int per_elems = 16 / esize;
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * (kThreadsLp / 64) + (threadIdx.x >> 6);
+    const bool row_ok = row < a.n;
+    const int p = lane % P, gl = lane / P;
+    const int G = a.G;
+    // unit (g, p) of the row is at g*P + p = lane + 64k for g = gl + GS*k
+    const uint4* wl = reinterpret_cast<const uint4*>(a.packed) + ((int64_t)(row_ok ? row : 0) * G * P + lane);
+    // decoded weights are +-2: half-scales; W planes multiply conj(x)
+    const float hr = 0.5f * a.scales[2 * p], hi = 0.5f * a.scales[2 * p + 1];
+    const float sg = (p < a.S) ? 1.0f : -1.0f;
+    const int pbytes = x_plane_bytes(XT, a.m64);
+    const int col_bytes = 2 * pbytes;
+
+    uint4 cur[2], nxt[2];
+    for (int b0 = 0; b0 < a.B; b0 += BCH) {
+        const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            cur[u] = (row_ok && gl + u * GS < G) ? wl[64 * u] : make_uint4(0, 0, 0, 0);
+        if (b0) __syncthreads();  // previous batch chunk fully read
+        for (int b = 0; b < nb; ++b)
+#pragma unroll
+            for (int pl = 0; pl < 2; ++pl) {
+                const uint8_t* src = reinterpret_cast<const uint8_t*>(pl ? a.x_im : a.x_re) +
+                                     (int64_t)(b0 + b) * a.ldx * esize;
+                uint8_t* dst = lds + (size_t)b * col_bytes + pl * pbytes;
+                for (int c = threadIdx.x * per_elems; c < a.m64; c += kThreadsLp * per_elems) {
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (c < a.m) v = *reinterpret_cast<const uint4*>(src + (size_t)c * esize);
+                    *reinterpret_cast<uint4*>(dst + x_col_off(XT, c)) = v;
+                }
+            }
+        __syncthreads();
+
+        float A[4][BCH];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int b = 0; b < BCH; ++b) A[q][b] = 0.f;
+        for (int g0 = gl; g0 < G; g0 += 2 * GS) {
+            // the next two units are in flight while these two are summed
+            const int gn = g0 + 2 * GS;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                nxt[u] = (row_ok && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + 64 * u] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int g = g0 + u * GS;
+                if (g < G) unit_accumulate<XT, BCH>(cur[u], 64 * g, lds, col_bytes, pbytes, nb, A);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) cur[u] = nxt[u];
+        }
+#pragma unroll
+        for (int b = 0; b < BCH; ++b) {
+            const float vr = group_sum<64>(hr * A[0][b] - sg * (hi * A[1][b]));
+            const float vi = group_sum<64>(sg * (hr * A[2][b]) + hi * A[3][b]);
+            if (lane == 0 && row_ok && b < nb) {
+                a.y_re[(int64_t)(b0 + b) * a.ldy + row] = vr;
+                a.y_im[(int64_t)(b0 + b) * a.ldy + row] = vi;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // int8 path: exact int32 accumulators per plane, reduced across lanes, then
 // the float epilogue from the exact sums.  A lane owns whole 64-column groups
@@ -406,10 +493,40 @@ hipError_t launch_units_bch(const GemvArgs& a, int bch, hipStream_t s)
     }
 }
 
+template <int XT, int P, int BCH>
+hipError_t launch_lp_t(const GemvArgs& a, hipStream_t s)
+{
+    const dim3 grid((a.n + (kThreadsLp / 64) - 1) / (kThreadsLp / 64));
+    const size_t lds = (size_t)x_bytes_per_col(XT, a.m64) * BCH;
+    hipLaunchKernelGGL((k_cgemv_lp<XT, P, BCH>), grid, dim3(kThreadsLp), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int XT, int P>
+hipError_t launch_lp_bch(const GemvArgs& a, int bch, hipStream_t s)
+{
+    switch (bch) {
+    case 8: return launch_lp_t<XT, P, 8>(a, s);
+    case 4: return launch_lp_t<XT, P, 4>(a, s);
+    case 2: return launch_lp_t<XT, P, 2>(a, s);
+    default: return launch_lp_t<XT, P, 1>(a, s);
+    }
+}
+
 template <int XT>
 hipError_t launch_float(const GemvArgs& a, hipStream_t s)
 {
     const int bch = pick_bch(XT, a.B, a.m64);
+    if (a.G * a.P >= 64) {
+        switch (a.P) {
+        case 1: return launch_lp_bch<XT, 1>(a, bch, s);
+        case 2: return launch_lp_bch<XT, 2>(a, bch, s);
+        case 4: return launch_lp_bch<XT, 4>(a, bch, s);
+        case 8: return launch_lp_bch<XT, 8>(a, bch, s);
+        case 16: return launch_lp_bch<XT, 16>(a, bch, s);
+        default: break;
+        }
+    }
     switch (pick_trow(a.G * a.P)) {
     case 64: return launch_units_bch<XT, 64>(a, bch, s);
     case 32: return launch_units_bch<XT, 32>(a, bch, s);

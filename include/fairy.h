@@ -183,6 +183,9 @@ size_t fairy_cgemv_workspace_bytes(const fairy_clinear* L, int32_t batch, int32_
  *                accumulators A1..A4 per plane (planes U_1..U_S, W_1..W_S).
  *   batch      : 1..64.
  *   workspace  : may be NULL when fairy_cgemv_workspace_bytes() is 0.
+ * The layer must be TILED64 with m % 16 == 0 and m <= 7680 (F32), 14528
+ * (BF16) or 26112 (I8): one batch column of activations is staged whole in
+ * 64 KiB of LDS.  Otherwise UNSUPPORTED.
  * float outputs are within 1e-5 relative L2 of the exact result on the same
  * inputs; integer accumulators are exact. */
 fairy_status fairy_cgemv(const fairy_clinear* L, const void* x_re, const void* x_im,

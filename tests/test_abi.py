@@ -152,6 +152,9 @@ def gemv(Lr, xr=A, xi=A, dt=F.FAIRY_BF16, B=1, ldx=64, yr=A, yi=A, ldy=64, acc=N
     ({"layout": F.FAIRY_LAYOUT_ROW16}, {}, F.FAIRY_ERR_UNSUPPORTED),
     ({"m": 72}, dict(ldx=80), F.FAIRY_ERR_UNSUPPORTED),     # m % 16
     ({"m": 16400}, dict(ldx=16400), F.FAIRY_ERR_UNSUPPORTED),
+    ({"m": 14592}, dict(ldx=14592), F.FAIRY_ERR_UNSUPPORTED),  # bf16 activations beyond 64 KiB of LDS
+    ({"m": 7744}, dict(ldx=7744, dt=F.FAIRY_F32), F.FAIRY_ERR_UNSUPPORTED),
+    ({"m": 26176}, dict(ldx=26176, dt=F.FAIRY_I8), F.FAIRY_ERR_UNSUPPORTED),
 ])
 def test_cgemv_validation(kw, call, want):
     assert gemv(layer(**kw), **call) == want

@@ -67,6 +67,11 @@ CASES = [
     (2, True, 130, 2048, 16),
     (2, True, 64, 5504, 4),
     (1, True, 20, 256, 64),
+    # one row per wave with lane-fixed planes (P | 64, >= 64 units per row)
+    (1, False, 7, 4112, 3),      # P = 1, ragged last group
+    (1, True, 33, 2064, 5),      # P = 2
+    (4, True, 19, 528, 6),       # P = 8
+    (8, True, 5, 272, 2),        # P = 16
 ]
 
 
@@ -93,6 +98,26 @@ def test_gemv_i8_exact(S, hc, n, m, B):
     assert np.array_equal(acc.astype(np.int64), oracle.cgemv_acc_i64(codes, xr, xi))
     wr, wi = oracle.cgemv_dense(codes, scales, S, hc, xr.astype(np.float64), xi.astype(np.float64))
     assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
+
+
+# the widest layers one staged activation column allows, two batch columns
+# (staged one at a time)
+@pytest.mark.parametrize("xdtype,m", [(F.FAIRY_BF16, 14528), (F.FAIRY_F32, 7680), (F.FAIRY_I8, 26112)])
+def test_gemv_max_m(xdtype, m):
+    S, hc, n, B = 2, True, 4, 2
+    log(f"gemv max m dt={xdtype} m={m}")
+    P = 2 * S
+    codes = synth.random_codes((P, n, m), 17 + m)
+    scales = synth.random_scales(P, 19 + m)
+    layer = layer_from_codes(codes, scales, S, hc)
+    if xdtype == F.FAIRY_I8:
+        xr, xi = synth.int8_uniform((B, m), 23)
+        yr, yi, acc = run_gemv(layer, dev(xr), dev(xi), xdtype, B, want_acc=True)
+        assert np.array_equal(acc.astype(np.int64), oracle.cgemv_acc_i64(codes, xr, xi))
+        wr, wi = oracle.cgemv_dense(codes, scales, S, hc, xr.astype(np.float64), xi.astype(np.float64))
+        assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
+    else:
+        check_float(layer, codes, scales, S, hc, B, xdtype, 29)
 
 
 def test_gemv_extreme_int8_values():
