@@ -24,6 +24,13 @@ int pick_bch(int xdtype, int B, int m64)
     return bch;
 }
 
+int pick_bch_lp(int xdtype, int B, int m64)
+{
+    int bch = B <= 1 ? 1 : B <= 4 ? 2 : 4;
+    while (bch > 1 && (size_t)x_bytes_per_col(xdtype, m64) * bch > 64 * 1024) bch /= 2;
+    return bch;
+}
+
 }  // namespace gemv
 
 namespace gemv {

@@ -267,6 +267,8 @@ __global__ __launch_bounds__(kThreads) void k_cgemv_units(GemvArgs a)
 // ---------------------------------------------------------------------------
 constexpr int kThreadsLp = 512;
 
+// blockIdx.y picks a chunk of BCH batch columns, so the chunks of a batch
+// run side by side (each re-reads the codes, from L2 after the first).
 template <int XT, int P, int BCH>
 __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
 {
@@ -280,62 +282,58 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
     const bool row_ok = row < a.n;
     const int p = lane % P, gl = lane / P;
     const int G = a.G;
+    const int b0 = blockIdx.y * BCH;
+    const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
     // unit (g, p) of the row is at g*P + p = lane + 64k for g = gl + GS*k
     const uint4* wl = reinterpret_cast<const uint4*>(a.packed) + ((int64_t)(row_ok ? row : 0) * G * P + lane);
+    uint4 cur[2], nxt[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) cur[u] = (row_ok && gl + u * GS < G) ? wl[64 * u] : make_uint4(0, 0, 0, 0);
     // decoded weights are +-2: half-scales; W planes multiply conj(x)
     const float hr = 0.5f * a.scales[2 * p], hi = 0.5f * a.scales[2 * p + 1];
     const float sg = (p < a.S) ? 1.0f : -1.0f;
     const int pbytes = x_plane_bytes(XT, a.m64);
     const int col_bytes = 2 * pbytes;
+    for (int b = 0; b < nb; ++b)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl) {
+            const uint8_t* src =
+                reinterpret_cast<const uint8_t*>(pl ? a.x_im : a.x_re) + (int64_t)(b0 + b) * a.ldx * esize;
+            uint8_t* dst = lds + (size_t)b * col_bytes + pl * pbytes;
+            for (int c = threadIdx.x * per_elems; c < a.m64; c += kThreadsLp * per_elems) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (c < a.m) v = *reinterpret_cast<const uint4*>(src + (size_t)c * esize);
+                *reinterpret_cast<uint4*>(dst + x_col_off(XT, c)) = v;
+            }
+        }
+    __syncthreads();
 
-    uint4 cur[2], nxt[2];
-    for (int b0 = 0; b0 < a.B; b0 += BCH) {
-        const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
+    float A[4][BCH];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < BCH; ++b) A[q][b] = 0.f;
+    for (int g0 = gl; g0 < G; g0 += 2 * GS) {
+        // the next two units are in flight while these two are summed
+        const int gn = g0 + 2 * GS;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            cur[u] = (row_ok && gl + u * GS < G) ? wl[64 * u] : make_uint4(0, 0, 0, 0);
-        if (b0) __syncthreads();  // previous batch chunk fully read
-        for (int b = 0; b < nb; ++b)
+            nxt[u] = (row_ok && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + 64 * u] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int pl = 0; pl < 2; ++pl) {
-                const uint8_t* src = reinterpret_cast<const uint8_t*>(pl ? a.x_im : a.x_re) +
-                                     (int64_t)(b0 + b) * a.ldx * esize;
-                uint8_t* dst = lds + (size_t)b * col_bytes + pl * pbytes;
-                for (int c = threadIdx.x * per_elems; c < a.m64; c += kThreadsLp * per_elems) {
-                    uint4 v = make_uint4(0, 0, 0, 0);
-                    if (c < a.m) v = *reinterpret_cast<const uint4*>(src + (size_t)c * esize);
-                    *reinterpret_cast<uint4*>(dst + x_col_off(XT, c)) = v;
-                }
-            }
-        __syncthreads();
-
-        float A[4][BCH];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int b = 0; b < BCH; ++b) A[q][b] = 0.f;
-        for (int g0 = gl; g0 < G; g0 += 2 * GS) {
-            // the next two units are in flight while these two are summed
-            const int gn = g0 + 2 * GS;
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                nxt[u] = (row_ok && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + 64 * u] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int g = g0 + u * GS;
-                if (g < G) unit_accumulate<XT, BCH>(cur[u], 64 * g, lds, col_bytes, pbytes, nb, A);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < 2; ++u) {
+            const int g = g0 + u * GS;
+            if (g < G) unit_accumulate<XT, BCH>(cur[u], 64 * g, lds, col_bytes, pbytes, nb, A);
         }
 #pragma unroll
-        for (int b = 0; b < BCH; ++b) {
-            const float vr = group_sum<64>(hr * A[0][b] - sg * (hi * A[1][b]));
-            const float vi = group_sum<64>(sg * (hr * A[2][b]) + hi * A[3][b]);
-            if (lane == 0 && row_ok && b < nb) {
-                a.y_re[(int64_t)(b0 + b) * a.ldy + row] = vr;
-                a.y_im[(int64_t)(b0 + b) * a.ldy + row] = vi;
-            }
+        for (int u = 0; u < 2; ++u) cur[u] = nxt[u];
+    }
+#pragma unroll
+    for (int b = 0; b < BCH; ++b) {
+        const float vr = group_sum<64>(hr * A[0][b] - sg * (hi * A[1][b]));
+        const float vi = group_sum<64>(sg * (hr * A[2][b]) + hi * A[3][b]);
+        if (lane == 0 && row_ok && b < nb) {
+            a.y_re[(int64_t)(b0 + b) * a.ldy + row] = vr;
+            a.y_im[(int64_t)(b0 + b) * a.ldy + row] = vi;
         }
     }
 }
@@ -496,7 +494,7 @@ hipError_t launch_units_bch(const GemvArgs& a, int bch, hipStream_t s)
 template <int XT, int P, int BCH>
 hipError_t launch_lp_t(const GemvArgs& a, hipStream_t s)
 {
-    const dim3 grid((a.n + (kThreadsLp / 64) - 1) / (kThreadsLp / 64));
+    const dim3 grid((a.n + (kThreadsLp / 64) - 1) / (kThreadsLp / 64), (a.B + BCH - 1) / BCH);
     const size_t lds = (size_t)x_bytes_per_col(XT, a.m64) * BCH;
     hipLaunchKernelGGL((k_cgemv_lp<XT, P, BCH>), grid, dim3(kThreadsLp), lds, s, a);
     return hipGetLastError();
@@ -506,24 +504,29 @@ template <int XT, int P>
 hipError_t launch_lp_bch(const GemvArgs& a, int bch, hipStream_t s)
 {
     switch (bch) {
-    case 8: return launch_lp_t<XT, P, 8>(a, s);
     case 4: return launch_lp_t<XT, P, 4>(a, s);
     case 2: return launch_lp_t<XT, P, 2>(a, s);
     default: return launch_lp_t<XT, P, 1>(a, s);
     }
 }
 
+// Batch columns per block of the one-row-per-wave kernel: wide enough to
+// share each decoded word among a few columns, narrow enough that a small
+// layer still has several waves per SIMD (the chunks run side by side).
+int pick_bch_lp(int xdtype, int B, int m64);
+
 template <int XT>
 hipError_t launch_float(const GemvArgs& a, hipStream_t s)
 {
     const int bch = pick_bch(XT, a.B, a.m64);
-    if (a.G * a.P >= 64) {
+    if (a.G * a.P >= 64 && a.B <= 64) {
+        const int bl = pick_bch_lp(XT, a.B, a.m64);
         switch (a.P) {
-        case 1: return launch_lp_bch<XT, 1>(a, bch, s);
-        case 2: return launch_lp_bch<XT, 2>(a, bch, s);
-        case 4: return launch_lp_bch<XT, 4>(a, bch, s);
-        case 8: return launch_lp_bch<XT, 8>(a, bch, s);
-        case 16: return launch_lp_bch<XT, 16>(a, bch, s);
+        case 1: return launch_lp_bch<XT, 1>(a, bl, s);
+        case 2: return launch_lp_bch<XT, 2>(a, bl, s);
+        case 4: return launch_lp_bch<XT, 4>(a, bl, s);
+        case 8: return launch_lp_bch<XT, 8>(a, bl, s);
+        case 16: return launch_lp_bch<XT, 16>(a, bl, s);
         default: break;
         }
     }
