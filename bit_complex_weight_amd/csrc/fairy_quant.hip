@@ -7,6 +7,8 @@
 // stream and allocate nothing.
 #include "fairy_internal.h"
 
+#include <type_traits>
+
 namespace fairy {
 namespace {
 
@@ -121,54 +123,74 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t count)
 // stage's exponent buckets (block-local LDS buckets, flushed once per block).
 // Stage k: recompute R_k from W with the scales of stages < k (already on
 // the device), write code_k, and add |R_k| on the code's axis into the
-// stage's exponent buckets.  Buckets live in LDS in kCopies interleaved copies
-// (lane % kCopies picks one) so lanes of a wave hitting the same exponent
-// rarely collide on one address; the copies are summed when the block flushes
-// its nonzero buckets to the workspace with integer atomics.
-constexpr int kCopies = 8;
+// stage's exponent buckets.  V = 4: each thread takes 4 consecutive elements
+// (float4 loads, one 32-bit store of 4 codes); V = 1 for unaligned arrays.
+// A block accumulates into kCopies interleaved LDS copies of the buckets,
+// then adds its nonzero buckets into global copy blockIdx % kGlobalCopies of
+// the stage's workspace (integer atomics: exact and order-independent; the
+// copies keep the blocks of a launch from contending on ~40 hot addresses).
+constexpr int kCopies = 2;
+constexpr int kGlobalCopies = 64;
+constexpr int kStageBlocks = 1024;
 
+template <int V>
 __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__ w_re,
                                                        const float* __restrict__ w_im, int64_t count,
                                                        int32_t k, const float* __restrict__ scales,
                                                        uint8_t* __restrict__ codes,
                                                        unsigned long long* __restrict__ ws)
 {
+    typedef typename std::conditional<V == 4, float4, float>::type vec_t;
+    typedef typename std::conditional<V == 4, uint32_t, uint8_t>::type code_t;
     __shared__ unsigned long long s_buck[kBuckets * kCopies];
     __shared__ unsigned long long s_cnt[2];
     for (int t = threadIdx.x; t < kBuckets * kCopies; t += blockDim.x) s_buck[t] = 0ull;
     if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0ull;
     __syncthreads();
 
-    const int lane = threadIdx.x & 63;
+    float sre[8], sim[8];
+    for (int j = 0; j < k; ++j) {
+        sre[j] = scales[2 * j];
+        sim[j] = scales[2 * j + 1];
+    }
     const int copy = threadIdx.x % kCopies;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < count; base += stride) {
-        const int64_t i = base + threadIdx.x;
-        const bool valid = i < count;
-        uint32_t axis = 0;
-        if (valid) {
-            float a = w_re[i], b = w_im[i];
-            for (int j = 0; j < k; ++j) residual_step(a, b, phase_code(a, b), scales[2 * j], scales[2 * j + 1]);
+    const int64_t nv = count / V;
+    const vec_t* vr = reinterpret_cast<const vec_t*>(w_re);
+    const vec_t* vi = reinterpret_cast<const vec_t*>(w_im);
+    code_t* cout = reinterpret_cast<code_t*>(codes + (int64_t)k * count);
+    uint32_t n_im = 0, n_all = 0;
+    for (int64_t iv = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; iv < nv;
+         iv += (int64_t)gridDim.x * blockDim.x) {
+        const vec_t ra = vr[iv], rb = vi[iv];
+        float av[V], bv[V];
+        if constexpr (V == 4) {
+            av[0] = ra.x; av[1] = ra.y; av[2] = ra.z; av[3] = ra.w;
+            bv[0] = rb.x; bv[1] = rb.y; bv[2] = rb.z; bv[3] = rb.w;
+        } else {
+            av[0] = ra;
+            bv[0] = rb;
+        }
+        uint32_t cpack = 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            float a = av[e], b = bv[e];
+            for (int j = 0; j < k; ++j) residual_step(a, b, phase_code(a, b), sre[j], sim[j]);
             const uint32_t c = phase_code(a, b);
-            codes[(int64_t)k * count + i] = (uint8_t)c;
-            axis = c & 1u;
+            cpack |= c << (8 * e);
+            const uint32_t axis = c & 1u;
+            n_im += axis;
             const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
             const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
             const uint32_t sig = ex ? (man | 0x800000u) : man;
             if (sig) atomicAdd(&s_buck[(axis * 256u + (ex ? ex : 1u)) * kCopies + copy], (unsigned long long)sig);
         }
-        // counts per axis: one ballot per wave instead of per-element atomics
-        const unsigned long long im_mask = __ballot(valid && axis == 1u);
-        const unsigned long long all_mask = __ballot(valid);
-        if (lane == 0) {
-            const unsigned long long n_im = __popcll(im_mask);
-            const unsigned long long n_all = __popcll(all_mask);
-            if (n_all - n_im) atomicAdd(&s_cnt[0], n_all - n_im);
-            if (n_im) atomicAdd(&s_cnt[1], n_im);
-        }
+        n_all += V;
+        cout[iv] = (code_t)cpack;
     }
+    if (n_all - n_im) atomicAdd(&s_cnt[0], (unsigned long long)(n_all - n_im));
+    if (n_im) atomicAdd(&s_cnt[1], (unsigned long long)n_im);
     __syncthreads();
-    unsigned long long* g = ws + (int64_t)k * kStageWords;
+    unsigned long long* g = ws + ((int64_t)k * kGlobalCopies + blockIdx.x % kGlobalCopies) * kStageWords;
     for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) {
         unsigned long long v = 0ull;
 #pragma unroll
@@ -188,32 +210,63 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
 // when E > 0, so Q1 plus that sticky bit decide the rounding exactly.
 constexpr int kLimbs = 10;  // 320 bits
 
-__global__ void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k, float* __restrict__ scales)
+constexpr int kFinThreads = 256;
+
+__global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k,
+                                                              float* __restrict__ scales)
 {
-    __shared__ unsigned long long s_part[2][16];
-    __shared__ unsigned long long s_b[kBuckets];
-    const int axis = threadIdx.x >> 5;  // 2 x 32 threads
-    const int L = threadIdx.x & 31;
-    const unsigned long long* g = ws + (int64_t)k * kStageWords;
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) s_b[t] = g[t];  // one parallel read
+    // 128 threads per axis; thread j splits buckets 2j and 2j+1 into 32-bit
+    // limb pieces, then a tree in LDS adds each limb over the 128 threads
+    // (fixed order, integer: exact)
+    __shared__ unsigned long long s_red[kFinThreads][kLimbs];
+    __shared__ unsigned long long s_part[2][kLimbs];
+    __shared__ unsigned long long s_b[kStageWords];
+    const int axis = threadIdx.x >> 7;
+    const int j = threadIdx.x & 127;
+    // buckets and counts: the sum of the stage's global copies
+    const unsigned long long* g0 = ws + (int64_t)k * kGlobalCopies * kStageWords;
+    for (int t = threadIdx.x; t < kStageWords; t += blockDim.x) {
+        unsigned long long v = 0ull;
+        for (int c = 0; c < kGlobalCopies; ++c) v += g0[(int64_t)c * kStageWords + t];
+        s_b[t] = v;
+    }
     __syncthreads();
-    const unsigned long long* buck = s_b + 256 * axis;
-    // thread L sums the 32-bit slices of every bucket that land in limb L
-    if (L < kLimbs) {
-        unsigned long long acc = 0ull;
-        for (int eb = 1; eb < 256; ++eb) {
-            const unsigned long long v = buck[eb];
-            if (!v) continue;
-            const int sh = eb - 1 - 32 * L;  // v * 2^(eb-1) seen from bit 32L
+    const unsigned long long* g = s_b;
+    unsigned long long part[kLimbs];
+#pragma unroll
+    for (int q = 0; q < kLimbs; ++q) part[q] = 0ull;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int eb = 2 * j + h;
+        const unsigned long long v = (eb >= 1) ? g[256 * axis + eb] : 0ull;
+        if (!v) continue;
+        // v * 2^(eb-1), seen limb by limb (limb q holds bits 32q .. 32q+31)
+#pragma unroll
+        for (int q = 0; q < kLimbs; ++q) {
+            const int sh = eb - 1 - 32 * q;
             uint32_t piece;
             if (sh >= 32 || sh <= -64) piece = 0u;
             else if (sh >= 0) piece = (uint32_t)(v << sh);
             else piece = (uint32_t)(v >> (-sh));
-            acc += piece;
+            part[q] += piece;
         }
-        s_part[axis][L] = acc;
+    }
+#pragma unroll
+    for (int q = 0; q < kLimbs; ++q) s_red[threadIdx.x][q] = part[q];
+    __syncthreads();
+    for (int w = 64; w >= 1; w >>= 1) {
+        if (j < w) {
+#pragma unroll
+            for (int q = 0; q < kLimbs; ++q) s_red[threadIdx.x][q] += s_red[threadIdx.x + w][q];
+        }
+        __syncthreads();
+    }
+    if (j == 0) {
+#pragma unroll
+        for (int q = 0; q < kLimbs; ++q) s_part[axis][q] = s_red[threadIdx.x][q];
     }
     __syncthreads();
+    const int L = j;
     if (L != 0) return;
     const unsigned long long cnt = g[kBuckets + axis];
     float result = 0.0f;
@@ -399,23 +452,31 @@ hipError_t launch_real_to_complex(const float* R, int64_t n, int64_t m, float* u
     return hipGetLastError();
 }
 
-size_t phasequant_workspace_bytes(int32_t stages) { return (size_t)stages * kStageWords * sizeof(unsigned long long); }
+size_t phasequant_workspace_bytes(int32_t stages)
+{
+    return (size_t)stages * kGlobalCopies * kStageWords * sizeof(unsigned long long);
+}
 
 hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count, int32_t stages,
                              uint8_t* codes, float* scales, float* resid_re, float* resid_im,
                              void* workspace, hipStream_t s)
 {
     unsigned long long* ws = (unsigned long long*)workspace;
-    const int64_t nws = (int64_t)stages * kStageWords;
-    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nws, kThreads, 64)), dim3(kThreads), 0, s, ws, nws);
+    const int64_t nws = (int64_t)stages * kGlobalCopies * kStageWords;
+    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(nws, kThreads, 256)), dim3(kThreads), 0, s, ws, nws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int grid = grid_for(count, kThreads, 2048);
+    const bool vec = count % 4 == 0 && ((((uintptr_t)w_re) | ((uintptr_t)w_im) | ((uintptr_t)codes)) % 16 == 0);
+    const int grid = grid_for(vec ? count / 4 : count, kThreads, kStageBlocks);
     for (int32_t k = 0; k < stages; ++k) {
-        hipLaunchKernelGGL(k_pq_stage, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, k,
-                           (const float*)scales, codes, ws);
+        if (vec)
+            hipLaunchKernelGGL(k_pq_stage<4>, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, k,
+                               (const float*)scales, codes, ws);
+        else
+            hipLaunchKernelGGL(k_pq_stage<1>, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, k,
+                               (const float*)scales, codes, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_pq_finalize, dim3(1), dim3(64), 0, s, (const unsigned long long*)ws, k, scales);
+        hipLaunchKernelGGL(k_pq_finalize, dim3(1), dim3(kFinThreads), 0, s, (const unsigned long long*)ws, k, scales);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (resid_re || resid_im) {

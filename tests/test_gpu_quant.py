@@ -46,6 +46,7 @@ def _check_pq(re, im, stages):
     ((1,), 1.0, 5, 1), ((7,), 1.0, 6, 3), ((1000, 3), 0.5, 7, 2),
     ((2048, 2048), 0.02 / np.sqrt(2), 9, 2),
     ((300, 77), 1.0, 10, 8),
+    ((2049, 3), 0.3, 11, 3),          # odd count: the one-element-per-thread path, many blocks
 ])
 def test_phasequant_bit_exact(shape, sigma, seed, stages):
     re, im = synth.complex_gaussian(shape, sigma, seed)
