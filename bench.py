@@ -291,6 +291,15 @@ def main():
         rows_out["phasequant_S2_2048x2048"] = {"ms": ms_q, "unique_GB/s": (count * 8) / (ms_q * 1e-3) / 1e9}
         ms_p = bn.ev_time(lambda i: F.fairy_pack(codes, P, n, m, F.FAIRY_LAYOUT_TILED64, L["packed"]), 20)
         rows_out["pack_P4_2048x2048"] = {"ms": ms_p, "GB/s": (P * count * 1.25) / (ms_p * 1e-3) / 1e9}
+        # the whole conversion (split, PhaseQuant of U and W, pack) in one call
+        q_packed, q_scales = torch.empty_like(L["packed"]), torch.empty_like(L["scales"])
+        wsq = F.fairy_quantize_workspace_bytes(n, m, S, 1)
+        wq = torch.empty(wsq, dtype=torch.uint8, device="cuda")
+        ms_r = bn.ev_time(lambda i: F.fairy_quantize_real(R, n, m, S, q_packed, q_scales, wq, wsq), 10)
+        if not (torch.equal(q_packed, L["packed"]) and torch.equal(q_scales, L["scales"])):
+            raise SystemExit("fairy_quantize_real differs from the step-by-step conversion")
+        rows_out["quantize_real_4096x4096_S2"] = {"ms": ms_r, "R_GB/s": (4 * n * m * 4) / (ms_r * 1e-3) / 1e9}
+        del wq
         for bb in (4, 16, 64):
             msb = bn.gemv_rate(L, descs, bb, F.FAIRY_BF16, steps=100)
             rows_out[f"gemv_2048x2048_bf16_B{bb}"] = {

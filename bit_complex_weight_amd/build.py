@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfairy.so")
 SOURCES = ["fairy_api.hip", "fairy_quant.hip", "fairy_gemv.hip", "fairy_gemv_bf16.hip",
-           "fairy_gemv_f32.hip", "fairy_gemv_i8.hip", "fairy_gemm.hip", "fairy_gemm_mfma.hip"]
+           "fairy_gemv_f32.hip", "fairy_gemv_i8.hip", "fairy_gemm.hip", "fairy_gemm_mfma.hip",
+           "fairy_layer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

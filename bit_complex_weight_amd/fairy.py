@@ -49,6 +49,15 @@ class fairy_clinear(ctypes.Structure):
     ]
 
 
+class fairy_layer_info(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int64), ("m", ctypes.c_int64),
+        ("stages", ctypes.c_int32), ("has_conj", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("planes", ctypes.c_int32),
+        ("packed_bytes", ctypes.c_uint64), ("header_bytes", ctypes.c_uint32),
+    ]
+
+
 _lib = None
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -95,6 +104,20 @@ def lib() -> ctypes.CDLL:
         L.fairy_cgemm.argtypes = [ctypes.POINTER(fairy_clinear), _p, _p, _i32, _i64, _i64, _p, _p, _i64, _p,
                                   _i32, _p, _sz, _p]
         L.fairy_cgemm.restype = _i32
+        L.fairy_quantize_workspace_bytes.argtypes = [_i64, _i64, _i32, _i32]
+        L.fairy_quantize_workspace_bytes.restype = _sz
+        L.fairy_quantize_real.argtypes = [_p, _i64, _i64, _i32, _p, _p, _p, _sz, _p]
+        L.fairy_quantize_real.restype = _i32
+        L.fairy_quantize_complex.argtypes = [_p, _p, _i64, _i64, _i32, _p, _p, _p, _sz, _p]
+        L.fairy_quantize_complex.restype = _i32
+        L.fairy_layer_file_bytes.argtypes = [_i64, _i64, _i32, _i32]
+        L.fairy_layer_file_bytes.restype = _sz
+        L.fairy_layer_save.argtypes = [ctypes.POINTER(fairy_clinear), _p, _sz, _p]
+        L.fairy_layer_save.restype = _i32
+        L.fairy_layer_read_info.argtypes = [_p, _sz, ctypes.POINTER(fairy_layer_info)]
+        L.fairy_layer_read_info.restype = _i32
+        L.fairy_layer_load.argtypes = [_p, _sz, _p, _p, _p]
+        L.fairy_layer_load.restype = _i32
         _lib = L
     return _lib
 
@@ -192,3 +215,50 @@ def fairy_cgemm(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc=None, algo=F
                 workspace_bytes=0, stream=None):
     _check(lib().fairy_cgemm(ctypes.byref(L), _ptr(x_re), _ptr(x_im), xdtype, M, ldx, _ptr(y_re), _ptr(y_im), ldy,
                              _ptr(acc), algo, _ptr(workspace), workspace_bytes, _stream(stream)), "fairy_cgemm")
+
+
+def fairy_quantize_workspace_bytes(n, m, stages, has_conj) -> int:
+    return lib().fairy_quantize_workspace_bytes(n, m, stages, has_conj)
+
+
+def fairy_quantize_real(R, n, m, stages, packed, scales, workspace, workspace_bytes, stream=None):
+    _check(lib().fairy_quantize_real(_ptr(R), n, m, stages, _ptr(packed), _ptr(scales), _ptr(workspace),
+                                     workspace_bytes, _stream(stream)), "fairy_quantize_real")
+
+
+def fairy_quantize_complex(w_re, w_im, n, m, stages, packed, scales, workspace, workspace_bytes, stream=None):
+    _check(lib().fairy_quantize_complex(_ptr(w_re), _ptr(w_im), n, m, stages, _ptr(packed), _ptr(scales),
+                                        _ptr(workspace), workspace_bytes, _stream(stream)), "fairy_quantize_complex")
+
+
+def fairy_layer_file_bytes(n, m, stages, has_conj) -> int:
+    return lib().fairy_layer_file_bytes(n, m, stages, has_conj)
+
+
+def _host_buf(buf):
+    """A writable or readable host buffer (bytearray, bytes, numpy array) ->
+    (address, size); the caller keeps it alive."""
+    if isinstance(buf, (bytes, bytearray)):
+        c = (ctypes.c_char * len(buf)).from_buffer(buf) if isinstance(buf, bytearray) else ctypes.c_char_p(buf)
+        return ctypes.cast(c, ctypes.c_void_p).value, len(buf)
+    iface = getattr(buf, "__array_interface__", None)
+    if iface is not None:
+        return iface["data"][0], buf.nbytes
+    raise TypeError(f"expected bytes, bytearray or a numpy array, got {type(buf).__name__}")
+
+
+def fairy_layer_save(L, buf, stream=None):
+    addr, size = _host_buf(buf)
+    _check(lib().fairy_layer_save(ctypes.byref(L), addr, size, _stream(stream)), "fairy_layer_save")
+
+
+def fairy_layer_read_info(buf) -> fairy_layer_info:
+    addr, size = _host_buf(buf)
+    info = fairy_layer_info()
+    _check(lib().fairy_layer_read_info(addr, size, ctypes.byref(info)), "fairy_layer_read_info")
+    return info
+
+
+def fairy_layer_load(buf, packed, scales, stream=None):
+    addr, size = _host_buf(buf)
+    _check(lib().fairy_layer_load(addr, size, _ptr(packed), _ptr(scales), _stream(stream)), "fairy_layer_load")

@@ -206,6 +206,74 @@ fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x
                          float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Whole-layer conversion on the device ----------------------------------
+ * [Fairy2i article §2.1 (widely-linear split), §3.1-§3.2 (PhaseQuant codes and
+ * axis scales), §4.1 (recursive residual stages)]: the steps above chained on
+ * `stream` with every intermediate in `workspace`, ending in TILED64 words.
+ *
+ * Workspace bytes for a conversion (0 for invalid arguments): has_conj = 1
+ * for fairy_quantize_real, 0 for fairy_quantize_complex. */
+size_t fairy_quantize_workspace_bytes(int64_t n, int64_t m, int32_t stages, int32_t has_conj);
+
+/* R: device fp32 [2n][2m], row-major.  Output: a widely-linear layer with
+ * P = 2S planes U_1..U_S, W_1..W_S,
+ *   packed : device, fairy_packed_words(n, m, 2S, TILED64) words, 16-byte aligned;
+ *   scales : device float [2S][2].
+ * Bit-identical to fairy_real_to_complex, fairy_phasequant on U and on W,
+ * and fairy_pack(TILED64) called in turn.  n*m < 2^32, 1 <= S <= 8;
+ * m % 16 == 0 (else UNSUPPORTED); workspace 256-byte aligned, at least
+ * fairy_quantize_workspace_bytes(n, m, S, 1) (else ERR_WORKSPACE). */
+fairy_status fairy_quantize_real(const float* R, int64_t n, int64_t m, int32_t stages,
+                                 uint32_t* packed, float* scales,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* w_re, w_im: device fp32 [n][m] of a complex layer; output P = S planes
+ * (no conjugate branch).  Same rules, workspace from
+ * fairy_quantize_workspace_bytes(n, m, S, 0). */
+fairy_status fairy_quantize_complex(const float* w_re, const float* w_im, int64_t n, int64_t m,
+                                    int32_t stages, uint32_t* packed, float* scales,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Serialised quantised layer ------------------------------------------------
+ * This library's own format (the pages define none), little-endian:
+ *   offset  bytes  field
+ *        0      8  magic, the ASCII bytes "FAIRYQL1"
+ *        8      4  uint32 format version (1)
+ *       12      4  uint32 header bytes H = 64 + 8P rounded up to a multiple of 64
+ *       16      8  int64 n          24  8  int64 m
+ *       32      4  int32 stages S   36  4  int32 has_conj
+ *       40      4  int32 layout (FAIRY_LAYOUT_TILED64)
+ *       44      4  int32 planes P = S (1 + has_conj)
+ *       48      8  uint64 packed bytes (4 * fairy_packed_words(n, m, P, layout))
+ *       56      8  zero
+ *       64     8P  float scales [P][2]; zero up to H
+ *        H         the packed words, exactly as the kernels read them.
+ * Buffers are host memory owned by the caller. */
+typedef struct {
+    int64_t n, m;
+    int32_t stages, has_conj, layout, planes;
+    uint64_t packed_bytes;
+    uint32_t header_bytes;
+} fairy_layer_info;
+
+/* Size of the file of a TILED64 layer (0 for invalid arguments or m % 16 != 0). */
+size_t fairy_layer_file_bytes(int64_t n, int64_t m, int32_t stages, int32_t has_conj);
+
+/* Writes the file of layer L (device data) into host buffer `buf` of
+ * `bytes` (ERR_WORKSPACE if too small).  Copies on `stream` and waits for it. */
+fairy_status fairy_layer_save(const fairy_clinear* L, void* buf, size_t bytes, void* stream);
+
+/* Reads and checks a header: magic, version (other versions: UNSUPPORTED),
+ * sizes consistent with each other and with `bytes`.  Host only; touches no
+ * device. */
+fairy_status fairy_layer_read_info(const void* buf, size_t bytes, fairy_layer_info* info);
+
+/* Copies the scales and packed words of a checked file into device buffers
+ * (packed 16-byte aligned, fairy_layer_info.packed_bytes; scales [P][2]);
+ * copies on `stream` and waits for it. */
+fairy_status fairy_layer_load(const void* buf, size_t bytes, uint32_t* packed, float* scales,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif
