@@ -47,6 +47,9 @@ def lib():
         L.orc_cgemv_dense.argtypes = [_p, _p, _i32, _i32, _i64, _i64, _p, _p, _i32, _i64, _p, _p, _i64]
         L.orc_cgemv_acc.argtypes = [_p, _p, _i32, _i32, _i64, _i64, _p, _p, _i32, _i64, _p, _p, _p, _i64]
         L.orc_cgemv_acc_i64.argtypes = [_p, _i32, _i64, _i64, _p, _p, _i32, _i64, _p]
+        L.orc_cattn_scores.argtypes = [_p, _p, _p, _p, _i32, _i64, _i64, _i32, ctypes.c_double, _i32, _p]
+        L.orc_cattention.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i64, _i64, _i32, ctypes.c_double, _i32,
+                                     _p, _p]
         _lib = L
     return _lib
 
@@ -170,3 +173,35 @@ def cgemv_acc_i64(codes, x_re, x_im):
     acc = np.empty((P, 4, B, n), np.int64)
     lib().orc_cgemv_acc_i64(pc, P, n, m, pxr, pxi, B, m, acc.ctypes.data)
     return acc
+
+
+def _attn_args(q_re, q_im, k_re, k_im):
+    q_re, pqr = _c(q_re, np.float32)
+    q_im, pqi = _c(q_im, np.float32)
+    k_re, pkr = _c(k_re, np.float32)
+    k_im, pki = _c(k_im, np.float32)
+    heads, sq, d = q_re.shape
+    sk = k_re.shape[1]
+    assert q_im.shape == q_re.shape and k_re.shape == (heads, sk, d) and k_im.shape == k_re.shape
+    return (q_re, q_im, k_re, k_im), (pqr, pqi, pkr, pki), heads, sq, sk, d
+
+
+def cattn_scores(q_re, q_im, k_re, k_im, scale: float, causal: bool = False):
+    """[heads][sq][d] queries, [heads][sk][d] keys -> scores [heads][sq][sk] (float64)."""
+    keep, ptrs, heads, sq, sk, d = _attn_args(q_re, q_im, k_re, k_im)
+    s = np.empty((heads, sq, sk), np.float64)
+    lib().orc_cattn_scores(*ptrs, heads, sq, sk, d, float(scale), int(bool(causal)), s.ctypes.data)
+    return s
+
+
+def cattention(q_re, q_im, k_re, k_im, v_re, v_im, scale: float, causal: bool = False):
+    """Complex attention forward -> (o_re, o_im) [heads][sq][d] (float64)."""
+    keep, ptrs, heads, sq, sk, d = _attn_args(q_re, q_im, k_re, k_im)
+    v_re, pvr = _c(v_re, np.float32)
+    v_im, pvi = _c(v_im, np.float32)
+    assert v_re.shape == (heads, sk, d) and v_im.shape == v_re.shape
+    o_re = np.empty((heads, sq, d), np.float64)
+    o_im = np.empty((heads, sq, d), np.float64)
+    lib().orc_cattention(*ptrs, pvr, pvi, heads, sq, sk, d, float(scale), int(bool(causal)), o_re.ctypes.data,
+                         o_im.ctypes.data)
+    return o_re, o_im

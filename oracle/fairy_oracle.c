@@ -424,3 +424,72 @@ void orc_cgemv_acc_i64(const uint8_t* codes, int32_t planes, int64_t n, int64_t 
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Complex attention  [iFairy press article §三; Fairy2i article §2.2]      */
+/* ------------------------------------------------------------------------ */
+/* score(i, j) = scale * Re( sum_d q[i][d] * conj(k[j][d]) ), written with
+ * complex arithmetic exactly as the definition reads; the softmax is the
+ * textbook one (subtract the row maximum, exponentiate, normalise). */
+static int orc_masked(int32_t causal, int64_t i, int64_t j, int64_t sq, int64_t sk)
+{
+    return causal && j > i + (sk - sq);
+}
+
+void orc_cattn_scores(const float* q_re, const float* q_im, const float* k_re, const float* k_im,
+                      int32_t heads, int64_t sq, int64_t sk, int32_t d, double scale, int32_t causal,
+                      double* s)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t h = 0; h < heads; ++h)
+        for (int64_t i = 0; i < sq; ++i) {
+            const int64_t qo = ((int64_t)h * sq + i) * d;
+            for (int64_t j = 0; j < sk; ++j) {
+                double* out = s + ((int64_t)h * sq + i) * sk + j;
+                if (orc_masked(causal, i, j, sq, sk)) {
+                    *out = -INFINITY;
+                    continue;
+                }
+                const int64_t ko = ((int64_t)h * sk + j) * d;
+                double complex acc = 0.0;
+                for (int32_t t = 0; t < d; ++t) {
+                    const double complex q = (double)q_re[qo + t] + I * (double)q_im[qo + t];
+                    const double complex k = (double)k_re[ko + t] + I * (double)k_im[ko + t];
+                    acc += q * conj(k);
+                }
+                *out = scale * creal(acc);
+            }
+        }
+}
+
+void orc_cattention(const float* q_re, const float* q_im, const float* k_re, const float* k_im,
+                    const float* v_re, const float* v_im, int32_t heads, int64_t sq, int64_t sk, int32_t d,
+                    double scale, int32_t causal, double* o_re, double* o_im)
+{
+    double* s = (double*)malloc(sizeof(double) * (size_t)heads * (size_t)sq * (size_t)sk);
+    if (!s) abort();
+    orc_cattn_scores(q_re, q_im, k_re, k_im, heads, sq, sk, d, scale, causal, s);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t h = 0; h < heads; ++h)
+        for (int64_t i = 0; i < sq; ++i) {
+            const double* row = s + ((int64_t)h * sq + i) * sk;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < sk; ++j)
+                if (row[j] > mx) mx = row[j];
+            double den = 0.0;
+            for (int64_t j = 0; j < sk; ++j) den += (row[j] == -INFINITY) ? 0.0 : exp(row[j] - mx);
+            for (int32_t t = 0; t < d; ++t) {
+                double ar = 0.0, ai = 0.0;
+                for (int64_t j = 0; j < sk; ++j) {
+                    if (row[j] == -INFINITY) continue;
+                    const double p = exp(row[j] - mx) / den;
+                    const int64_t vo = ((int64_t)h * sk + j) * d + t;
+                    ar += p * (double)v_re[vo];   /* real and imaginary parts weighted separately */
+                    ai += p * (double)v_im[vo];
+                }
+                o_re[((int64_t)h * sq + i) * d + t] = ar;
+                o_im[((int64_t)h * sq + i) * d + t] = ai;
+            }
+        }
+    free(s);
+}

@@ -21,6 +21,8 @@
  *       §2.3.1 multiplying by i is a real/imag swap plus a negation.
  *   [iFairy abstract]  arXiv 2508.05571 record: every code has exactly one
  *       non-zero axis, so inference needs only additions and swaps.
+ *   [iFairy press article] bestcxt.com, §三: attention scores are the real
+ *       part of the Hermitian inner product (a real number for the softmax).
  *
  * Readings taken where the pages are silent are listed in the design doc and
  * repeated next to the function they affect.
@@ -105,6 +107,22 @@ void orc_cgemv_acc(const uint8_t* codes, const float* scales, int32_t stages, in
 void orc_cgemv_acc_i64(const uint8_t* codes, int32_t planes, int64_t n, int64_t m,
                        const int8_t* x_re, const int8_t* x_im, int32_t batch, int64_t ldx,
                        int64_t* acc);
+
+/* Complex attention  [iFairy press article §三; Fairy2i article §2.2;
+ * iFairy talk §2.1.4]: the similarity of query q and key k is the real part
+ * of their Hermitian inner product, Re(sum_d q_d conj(k_d)); a softmax over
+ * the keys turns the (scaled) scores into real weights, and the value
+ * vectors' real and imaginary parts are averaged with those weights.
+ *   q: [heads][sq][d], k, v: [heads][sk][d], split re/im planes (float);
+ *   causal != 0: query i sees keys j <= i + (sk - sq) only (sk >= sq).
+ * Scores: s [heads][sq][sk] = scale * Re(q . conj(k)), masked entries -inf.
+ * Output: o [heads][sq][d] (double). */
+void orc_cattn_scores(const float* q_re, const float* q_im, const float* k_re, const float* k_im,
+                      int32_t heads, int64_t sq, int64_t sk, int32_t d, double scale, int32_t causal,
+                      double* s);
+void orc_cattention(const float* q_re, const float* q_im, const float* k_re, const float* k_im,
+                    const float* v_re, const float* v_im, int32_t heads, int64_t sq, int64_t sk, int32_t d,
+                    double scale, int32_t causal, double* o_re, double* o_im);
 
 #ifdef __cplusplus
 }
