@@ -139,6 +139,18 @@ class Bench:
         ms, _ = self.graph_time(f, steps)
         return ms
 
+    def attention_rate(self, h, sq, sk, d, causal, iters=10, seed=205):
+        torch, F = self.torch, self.F
+        bufs = []
+        for i, rows in enumerate([sq, sq, sk, sk, sk, sk]):
+            bufs.append(self.dev(self.synth.bf16_bits(self.synth.gaussian((h, rows, d), 1.0, seed + i))))
+        o_re = torch.empty((h, sq, d), dtype=torch.float32, device="cuda")
+        o_im = torch.empty_like(o_re)
+        scale = 1.0 / math.sqrt(2 * d)
+        f = lambda i: F.fairy_cattention(*bufs, F.FAIRY_BF16, h, sq, sk, d, scale, causal, o_re, o_im)
+        f(0)
+        return attention_entry(self.ev_time(f, iters), h, sq, sk, d, causal)
+
     def gemm_rate(self, L, desc, M, xdtype, algo, iters=5, seed=204):
         torch, F = self.torch, self.F
         n, m = L["n"], L["m"]
@@ -152,6 +164,26 @@ class Bench:
         f = lambda i: F.fairy_cgemm(desc, xr, xi, xdtype, M, m, yr, yi, n, None, algo)
         f(0)
         return self.ev_time(f, iters)
+
+
+def attention_entry(ms, h, sq, sk, d, causal):
+    """Useful work: scores 4 sq sk d (the real-equivalent dot products over 2d)
+    plus the weighted sums 4 sq sk d (re and im); causal keeps the visible
+    (query, key) pairs.  Matrix-core work of the kernel: 12 sq sk d per
+    processed 64-key chunk (the weights go through two bf16 MFMAs)."""
+    if causal:
+        pairs = sum(min(sk, i + (sk - sq) + 1) for i in range(sq))
+        # a block of 64 queries walks the 64-key chunks up to its last query's diagonal
+        mfma_pairs = sum(((min(sk, qb * 64 + 64 + (sk - sq)) + 63) // 64) * 64 * 64
+                         for qb in range((sq + 63) // 64))
+    else:
+        pairs = sq * sk
+        mfma_pairs = ((sq + 63) // 64) * 64 * ((sk + 63) // 64) * 64
+    alg = 8.0 * h * pairs * d
+    mf = 12.0 * h * mfma_pairs * d
+    t = ms * 1e-3
+    return {"ms": ms, "alg_TFLOPs": alg / t / 1e12, "mfma_TFLOPs": mf / t / 1e12,
+            "mfma_frac": mf / t / 1e12 / MFMA_PEAK_TFLOPS["bf16"]}
 
 
 def gemm_entry(ms, P, n, m, M, peak=None):
@@ -336,6 +368,11 @@ def main():
             rows_out[f"gemm_2048x2048_M2048_{dn}_mfma"] = gemm_entry(msg, P, n, m, 2048, MFMA_PEAK_TFLOPS[dn])
             msg = bn.gemm_rate(L, d0, 2048, dt, F.FAIRY_ALGO_VALU, iters=2)
             rows_out[f"gemm_2048x2048_M2048_{dn}_valu"] = gemm_entry(msg, P, n, m, 2048)
+        # complex attention at the LLaMA-2-7B prefill shape: 32 heads, 2048
+        # tokens, real head dim 128 = complex d 64
+        for causal in (1, 0):
+            rows_out[f"cattention_32x2048_d64_{'causal' if causal else 'full'}"] = bn.attention_rate(
+                32, 2048, 2048, 64, causal)
         result["rows"] = rows_out
         log(json.dumps(rows_out))
 

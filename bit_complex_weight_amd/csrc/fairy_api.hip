@@ -210,4 +210,24 @@ fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x
     return from_hip(e);
 }
 
+fairy_status fairy_cattention(const void* q_re, const void* q_im, const void* k_re, const void* k_im,
+                              const void* v_re, const void* v_im, int32_t dtype, int32_t heads, int64_t sq,
+                              int64_t sk, int32_t d, float scale, int32_t causal, float* o_re, float* o_im,
+                              void* stream)
+{
+    const void* ptrs[8] = {q_re, q_im, k_re, k_im, v_re, v_im, o_re, o_im};
+    for (const void* p : ptrs)
+        if (!p || !aligned(p, 16)) return FAIRY_ERR_INVALID_ARG;
+    if (heads < 1 || heads > 65535 || sq < 1 || sk < 1 || sq > kMaxDim || sk > kMaxDim) return FAIRY_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FAIRY_ERR_INVALID_ARG;
+    if (causal && sk < sq) return FAIRY_ERR_INVALID_ARG;
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f) return FAIRY_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return FAIRY_ERR_INVALID_ARG;
+    if (dtype != FAIRY_BF16) return FAIRY_ERR_UNSUPPORTED;
+    if (d != 32 && d != 64 && d != 128) return FAIRY_ERR_UNSUPPORTED;
+    clear_stale_error();
+    return from_hip(fairy::launch_cattention(q_re, q_im, k_re, k_im, v_re, v_im, heads, sq, sk, d, scale, causal,
+                                             o_re, o_im, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -119,4 +119,9 @@ hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, 
                         int64_t M, int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc,
                         int32_t algo, void* workspace, hipStream_t s);
 
+// complex attention forward (fairy_attention.hip); bf16 inputs, d in {32, 64, 128}
+hipError_t launch_cattention(const void* q_re, const void* q_im, const void* k_re, const void* k_im,
+                             const void* v_re, const void* v_im, int32_t heads, int64_t sq, int64_t sk, int32_t d,
+                             float scale, int32_t causal, float* o_re, float* o_im, hipStream_t s);
+
 }  // namespace fairy

@@ -118,6 +118,9 @@ def lib() -> ctypes.CDLL:
         L.fairy_layer_read_info.restype = _i32
         L.fairy_layer_load.argtypes = [_p, _sz, _p, _p, _p]
         L.fairy_layer_load.restype = _i32
+        L.fairy_cattention.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i64, _i32, ctypes.c_float, _i32,
+                                       _p, _p, _p]
+        L.fairy_cattention.restype = _i32
         _lib = L
     return _lib
 
@@ -262,3 +265,10 @@ def fairy_layer_read_info(buf) -> fairy_layer_info:
 def fairy_layer_load(buf, packed, scales, stream=None):
     addr, size = _host_buf(buf)
     _check(lib().fairy_layer_load(addr, size, _ptr(packed), _ptr(scales), _stream(stream)), "fairy_layer_load")
+
+
+def fairy_cattention(q_re, q_im, k_re, k_im, v_re, v_im, dtype, heads, sq, sk, d, scale, causal, o_re, o_im,
+                     stream=None):
+    _check(lib().fairy_cattention(_ptr(q_re), _ptr(q_im), _ptr(k_re), _ptr(k_im), _ptr(v_re), _ptr(v_im), dtype,
+                                  heads, sq, sk, d, float(scale), int(causal), _ptr(o_re), _ptr(o_im),
+                                  _stream(stream)), "fairy_cattention")

@@ -274,6 +274,27 @@ fairy_status fairy_layer_read_info(const void* buf, size_t bytes, fairy_layer_in
 fairy_status fairy_layer_load(const void* buf, size_t bytes, uint32_t* packed, float* scales,
                               void* stream);
 
+/* ---- Complex attention -------------------------------------------------------
+ * [iFairy press article §三; Fairy2i article §2.2; iFairy talk §2.1.4]
+ *   score(i, j) = scale * Re(sum_t q[i][t] conj(k[j][t]))
+ *              (= scale * (q_re . k_re + q_im . k_im), the real dot product of
+ *                 the concatenated [re | im] vectors)
+ *   w(i, .)    = softmax over the keys j (causal: only j <= i + sk - sq)
+ *   o[i][t]    = sum_j w(i, j) v[j][t], real and imaginary parts separately.
+ *   q_re, q_im       : device bf16 [heads][sq][d];  k_*, v_* : bf16 [heads][sk][d]
+ *   o_re, o_im       : device fp32 [heads][sq][d], overwritten
+ *   dtype            : FAIRY_BF16 (others UNSUPPORTED); d in {32, 64, 128}
+ *                      (else UNSUPPORTED); all pointers 16-byte aligned
+ *   causal           : 0 or 1; causal needs sk >= sq (INVALID_ARG otherwise)
+ * One fused pass on the matrix cores (online softmax, nothing of size
+ * sq x sk in memory).  Scores are exact fp32 sums of the bf16 products;
+ * the weights are carried to ~2^-17 relative precision, so o is within
+ * 2e-5 relative L2 of the exact result on the same bf16 inputs. */
+fairy_status fairy_cattention(const void* q_re, const void* q_im, const void* k_re, const void* k_im,
+                              const void* v_re, const void* v_im, int32_t dtype, int32_t heads,
+                              int64_t sq, int64_t sk, int32_t d, float scale, int32_t causal,
+                              float* o_re, float* o_im, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -121,3 +121,31 @@ def test_save_load_validation():
     assert _raw("fairy_layer_load", addr, size, None, A, None) == F.FAIRY_ERR_INVALID_ARG
     assert _raw("fairy_layer_load", addr, size, A + 4, A, None) == F.FAIRY_ERR_INVALID_ARG
     assert _raw("fairy_layer_load", addr, 40, A, A, None) == F.FAIRY_ERR_INVALID_ARG
+
+
+def test_cattention_validation():
+    """Argument checks of fairy_cattention (all fail before any device work)."""
+    f = F.lib().fairy_cattention
+    ok = dict(q=A, k=A, v=A, o=A, dt=F.FAIRY_BF16, h=2, sq=64, sk=64, d=64, scale=0.1, causal=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["q"], a["q"], a["k"], a["k"], a["v"], a["v"], a["dt"], a["h"], a["sq"], a["sk"], a["d"],
+                 a["scale"], a["causal"], a["o"], a["o"], None)
+
+    assert call(q=None) == F.FAIRY_ERR_INVALID_ARG
+    assert call(k=A + 8) == F.FAIRY_ERR_INVALID_ARG
+    assert call(o=None) == F.FAIRY_ERR_INVALID_ARG
+    assert call(h=0) == F.FAIRY_ERR_INVALID_ARG
+    assert call(h=70000) == F.FAIRY_ERR_INVALID_ARG
+    assert call(sq=0) == F.FAIRY_ERR_INVALID_ARG
+    assert call(sk=0) == F.FAIRY_ERR_INVALID_ARG
+    assert call(causal=2) == F.FAIRY_ERR_INVALID_ARG
+    assert call(causal=1, sq=65, sk=64) == F.FAIRY_ERR_INVALID_ARG     # causal needs sk >= sq
+    assert call(scale=float("nan")) == F.FAIRY_ERR_INVALID_ARG
+    assert call(dt=7) == F.FAIRY_ERR_INVALID_ARG
+    assert call(dt=F.FAIRY_F32) == F.FAIRY_ERR_UNSUPPORTED
+    assert call(dt=F.FAIRY_I8) == F.FAIRY_ERR_UNSUPPORTED
+    assert call(d=48) == F.FAIRY_ERR_UNSUPPORTED
+    assert call(d=256) == F.FAIRY_ERR_UNSUPPORTED
