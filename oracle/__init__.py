@@ -50,6 +50,7 @@ def lib():
         L.orc_cattn_scores.argtypes = [_p, _p, _p, _p, _i32, _i64, _i64, _i32, ctypes.c_double, _i32, _p]
         L.orc_cattention.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i64, _i64, _i32, ctypes.c_double, _i32,
                                      _p, _p]
+        L.orc_rope.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i32, ctypes.c_double]
         _lib = L
     return _lib
 
@@ -205,3 +206,14 @@ def cattention(q_re, q_im, k_re, k_im, v_re, v_im, scale: float, causal: bool = 
     lib().orc_cattention(*ptrs, pvr, pvi, heads, sq, sk, d, float(scale), int(bool(causal)), o_re.ctypes.data,
                          o_im.ctypes.data)
     return o_re, o_im
+
+
+def rope(y_re, y_im, positions, head_dim: int, base: float):
+    """y [rows][n] complex (two float arrays) -> rotated copies (float64)."""
+    y_re = np.array(np.atleast_2d(y_re), np.float64, order="C")
+    y_im = np.array(np.atleast_2d(y_im), np.float64, order="C")
+    pos, pp = _c(positions, np.int32)
+    rows, n = y_re.shape
+    assert pos.size == rows and y_im.shape == y_re.shape
+    lib().orc_rope(y_re.ctypes.data, y_im.ctypes.data, rows, n, n, pp, int(head_dim), float(base))
+    return y_re, y_im

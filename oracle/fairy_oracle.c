@@ -493,3 +493,20 @@ void orc_cattention(const float* q_re, const float* q_im, const float* k_re, con
         }
     free(s);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Complex rotary position encoding  [iFairy press article §三]             */
+/* ------------------------------------------------------------------------ */
+void orc_rope(double* y_re, double* y_im, int64_t rows, int64_t n, int64_t ld, const int32_t* pos,
+              int32_t head_dim, double base)
+{
+    for (int64_t b = 0; b < rows; ++b)
+        for (int64_t r = 0; r < n; ++r) {
+            const int64_t j = r % head_dim;
+            const double theta = pow(base, -(double)j / (double)head_dim);
+            const double complex rot = cexp(I * ((double)pos[b] * theta));
+            const double complex y = (y_re[b * ld + r] + I * y_im[b * ld + r]) * rot;
+            y_re[b * ld + r] = creal(y);
+            y_im[b * ld + r] = cimag(y);
+        }
+}

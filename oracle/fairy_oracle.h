@@ -124,6 +124,13 @@ void orc_cattention(const float* q_re, const float* q_im, const float* k_re, con
                     const float* v_re, const float* v_im, int32_t heads, int64_t sq, int64_t sk, int32_t d,
                     double scale, int32_t causal, double* o_re, double* o_im);
 
+/* Complex rotary position encoding  [iFairy press article §三; iFairy talk
+ * §2.1.3]: on the complex plane the rotation is one complex multiplication.
+ * y[b][r] <- y[b][r] * exp(i * pos[b] * theta_j), j = r % head_dim,
+ * theta_j = base^(-j / head_dim); y is [rows][ld] (double, in place). */
+void orc_rope(double* y_re, double* y_im, int64_t rows, int64_t n, int64_t ld, const int32_t* pos,
+              int32_t head_dim, double base);
+
 #ifdef __cplusplus
 }
 #endif
