@@ -5,6 +5,8 @@
 // are reported as fairy_status codes, never by exceptions or printing.
 #include "fairy_gemv_impl.h"
 
+#include <cmath>
+
 namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -205,6 +207,51 @@ fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x
     if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FAIRY_ERR_WORKSPACE;
     clear_stale_error();
     hipError_t e = fairy::launch_cgemm(la, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, algo, workspace,
+                                       as_stream(stream));
+    if (e == hipErrorNotSupported) return FAIRY_ERR_UNSUPPORTED;
+    return from_hip(e);
+}
+
+// Rotary position arguments: positions device int32 [rows], 4-byte aligned;
+// head_dim >= 1; base finite and > 0.
+static fairy_status check_rope(const int32_t* positions, int32_t head_dim, float base, fairy::LayerArgs* la)
+{
+    if (!positions || !aligned(positions, 4) || head_dim < 1) return FAIRY_ERR_INVALID_ARG;
+    if (!(base > 0.0f) || base > 3.0e38f) return FAIRY_ERR_INVALID_ARG;
+    la->rope_pos = positions;
+    la->rope_d = head_dim;
+    la->rope_log2_base = std::log2((double)base);
+    return FAIRY_OK;
+}
+
+fairy_status fairy_cgemv_rope(const fairy_clinear* L, const void* x_re, const void* x_im, int32_t xdtype,
+                              int32_t batch, int64_t ldx, float* y_re, float* y_im, int64_t ldy,
+                              const int32_t* positions, int32_t head_dim, float base, void* stream)
+{
+    if (batch < 1 || batch > 64) return FAIRY_ERR_INVALID_ARG;
+    fairy::LayerArgs la;
+    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, nullptr, &la);
+    if (st != FAIRY_OK) return st;
+    if ((st = check_rope(positions, head_dim, base, &la)) != FAIRY_OK) return st;
+    clear_stale_error();
+    return from_hip(fairy::launch_cgemv(la, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, nullptr,
+                                        as_stream(stream)));
+}
+
+fairy_status fairy_cgemm_rope(const fairy_clinear* L, const void* x_re, const void* x_im, int32_t xdtype,
+                              int64_t M, int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t algo,
+                              const int32_t* positions, int32_t head_dim, float base, void* stream)
+{
+    if (M < 1 || M > kMaxDim) return FAIRY_ERR_INVALID_ARG;
+    if (algo != FAIRY_ALGO_AUTO && algo != FAIRY_ALGO_VALU && algo != FAIRY_ALGO_MFMA) return FAIRY_ERR_INVALID_ARG;
+    fairy::LayerArgs la;
+    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, nullptr, &la);
+    if (st != FAIRY_OK) return st;
+    if (algo == FAIRY_ALGO_MFMA && xdtype == FAIRY_F32) return FAIRY_ERR_UNSUPPORTED;
+    if ((st = check_rope(positions, head_dim, base, &la)) != FAIRY_OK) return st;
+    if (fairy::cgemm_workspace_bytes(la, M, xdtype, algo)) return FAIRY_ERR_UNSUPPORTED;
+    clear_stale_error();
+    hipError_t e = fairy::launch_cgemm(la, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, nullptr, algo, nullptr,
                                        as_stream(stream));
     if (e == hipErrorNotSupported) return FAIRY_ERR_UNSUPPORTED;
     return from_hip(e);

@@ -252,8 +252,11 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
                 if (row < a.n && tok < a.B) {
                     float* yr = a.y_re + (int64_t)tok * a.ldy + row;
                     float* yi = a.y_im + (int64_t)tok * a.ldy + row;
-                    *yr = accumulate ? *yr + pr[tt][rt][v] : pr[tt][rt][v];
-                    *yi = accumulate ? *yi + pi[tt][rt][v] : pi[tt][rt][v];
+                    float fr = accumulate ? *yr + pr[tt][rt][v] : pr[tt][rt][v];
+                    float fi = accumulate ? *yi + pi[tt][rt][v] : pi[tt][rt][v];
+                    gemv::rope_apply(a, row, tok, fr, fi);  // set on the last pass only
+                    *yr = fr;
+                    *yi = fi;
                 }
             }
         }
@@ -367,16 +370,13 @@ hipError_t launch_all(const GemvArgs& a, hipStream_t s)
     for (int p0 = 0; p0 < a.P && e == hipSuccess;) {
         const int rem = a.P - p0;
         const int acc = p0 > 0;
-        if (rem >= 4) {
-            e = launch_pass<XT, 4>(a, p0, acc, s);
-            p0 += 4;
-        } else if (rem >= 2) {
-            e = launch_pass<XT, 2>(a, p0, acc, s);
-            p0 += 2;
-        } else {
-            e = launch_pass<XT, 1>(a, p0, acc, s);
-            p0 += 1;
-        }
+        const int q = rem >= 4 ? 4 : rem >= 2 ? 2 : 1;
+        GemvArgs pass = a;
+        if (p0 + q < a.P) pass.pos = nullptr;  // the rotation applies to the finished sum
+        if (q == 4) e = launch_pass<XT, 4>(pass, p0, acc, s);
+        else if (q == 2) e = launch_pass<XT, 2>(pass, p0, acc, s);
+        else e = launch_pass<XT, 1>(pass, p0, acc, s);
+        p0 += q;
     }
     return e;
 }

@@ -54,6 +54,9 @@ GemvArgs make_args(const LayerArgs& L, const void* x_re, const void* x_im, int64
     a.S = L.stages;
     a.P = L.planes;
     a.B = (int32_t)batch;
+    a.pos = L.rope_pos;
+    a.rope_d = L.rope_d;
+    a.rope_log2_base = L.rope_log2_base;
     return a;
 }
 }  // namespace gemv

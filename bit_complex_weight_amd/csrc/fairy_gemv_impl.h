@@ -53,7 +53,30 @@ struct GemvArgs {
     int32_t* acc;
     int64_t ldx, ldy;
     int32_t n, m, m64, G, S, P, B;
+    // optional rotary position encoding of the outputs (pos == nullptr: none)
+    const int32_t* pos;
+    int32_t rope_d;
+    double rope_log2_base;
 };
+
+// Complex rotary position encoding of an output [iFairy press article §三;
+// iFairy talk §2.1.3: on the complex plane the rotation is one complex
+// multiplication]: complex dimension j = row % rope_d of batch column (or
+// token) b is multiplied by exp(i pos[b] theta_j), theta_j = base^(-j/rope_d).
+// Angles and the rotation are evaluated in fp64: in fp32, pos * theta would
+// already be off by ~1e-4 rad at positions in the thousands.
+__device__ __forceinline__ void rope_apply(const GemvArgs& a, int64_t row, int64_t b, float& vr, float& vi)
+{
+    if (!a.pos) return;
+    const int64_t j = row % a.rope_d;
+    const double theta = exp2(-((double)j / (double)a.rope_d) * a.rope_log2_base);
+    const double ang = (double)a.pos[b] * theta;
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const double xr = vr, xi = vi;
+    vr = (float)(xr * cs - xi * sn);
+    vi = (float)(xr * sn + xi * cs);
+}
 
 constexpr int kThreads = 256;
 constexpr int kScaleBytes = 128;  // LDS prefix holding up to 16 planes x 2 half-scales
@@ -250,9 +273,10 @@ __global__ __launch_bounds__(kThreads) void k_cgemv_units(GemvArgs a)
         }
 #pragma unroll
         for (int b = 0; b < BCH; ++b) {
-            const float sr = group_sum<TROW>(yr[b]);
-            const float si = group_sum<TROW>(yi[b]);
+            float sr = group_sum<TROW>(yr[b]);
+            float si = group_sum<TROW>(yi[b]);
             if (lr == 0 && row_ok && b < nb) {
+                rope_apply(a, row, b0 + b, sr, si);
                 a.y_re[(int64_t)(b0 + b) * a.ldy + row] = sr;
                 a.y_im[(int64_t)(b0 + b) * a.ldy + row] = si;
             }
@@ -329,9 +353,10 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
     }
 #pragma unroll
     for (int b = 0; b < BCH; ++b) {
-        const float vr = group_sum<64>(hr * A[0][b] - sg * (hi * A[1][b]));
-        const float vi = group_sum<64>(sg * (hr * A[2][b]) + hi * A[3][b]);
+        float vr = group_sum<64>(hr * A[0][b] - sg * (hi * A[1][b]));
+        float vi = group_sum<64>(sg * (hr * A[2][b]) + hi * A[3][b]);
         if (lane == 0 && row_ok && b < nb) {
+            rope_apply(a, row, b0 + b, vr, vi);
             a.y_re[(int64_t)(b0 + b) * a.ldy + row] = vr;
             a.y_im[(int64_t)(b0 + b) * a.ldy + row] = vi;
         }
@@ -457,6 +482,7 @@ __global__ __launch_bounds__(kThreads) void k_cgemv_i8(GemvArgs a)
                 }
             }
             if (lr == 0 && row_ok && b < nb) {
+                rope_apply(a, row, b0 + b, yr, yi);
                 a.y_re[(int64_t)(b0 + b) * a.ldy + row] = yr;
                 a.y_im[(int64_t)(b0 + b) * a.ldy + row] = yi;
             }

@@ -108,6 +108,10 @@ struct LayerArgs {
     const float* scales;
     int64_t n, m;
     int32_t stages, planes;
+    // optional rotary position encoding of the outputs (rope_pos == nullptr: none)
+    const int32_t* rope_pos = nullptr;
+    int32_t rope_d = 1;
+    double rope_log2_base = 0.0;
 };
 
 hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype,

@@ -121,6 +121,12 @@ def lib() -> ctypes.CDLL:
         L.fairy_cattention.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i64, _i64, _i32, ctypes.c_float, _i32,
                                        _p, _p, _p]
         L.fairy_cattention.restype = _i32
+        L.fairy_cgemv_rope.argtypes = [ctypes.POINTER(fairy_clinear), _p, _p, _i32, _i32, _i64, _p, _p, _i64, _p, _i32,
+                                       ctypes.c_float, _p]
+        L.fairy_cgemv_rope.restype = _i32
+        L.fairy_cgemm_rope.argtypes = [ctypes.POINTER(fairy_clinear), _p, _p, _i32, _i64, _i64, _p, _p, _i64, _i32, _p,
+                                       _i32, ctypes.c_float, _p]
+        L.fairy_cgemm_rope.restype = _i32
         _lib = L
     return _lib
 
@@ -272,3 +278,15 @@ def fairy_cattention(q_re, q_im, k_re, k_im, v_re, v_im, dtype, heads, sq, sk, d
     _check(lib().fairy_cattention(_ptr(q_re), _ptr(q_im), _ptr(k_re), _ptr(k_im), _ptr(v_re), _ptr(v_im), dtype,
                                   heads, sq, sk, d, float(scale), int(causal), _ptr(o_re), _ptr(o_im),
                                   _stream(stream)), "fairy_cattention")
+
+
+def fairy_cgemv_rope(L, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, positions, head_dim, base, stream=None):
+    _check(lib().fairy_cgemv_rope(ctypes.byref(L), _ptr(x_re), _ptr(x_im), xdtype, batch, ldx, _ptr(y_re),
+                                  _ptr(y_im), ldy, _ptr(positions), head_dim, float(base), _stream(stream)),
+           "fairy_cgemv_rope")
+
+
+def fairy_cgemm_rope(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, algo, positions, head_dim, base, stream=None):
+    _check(lib().fairy_cgemm_rope(ctypes.byref(L), _ptr(x_re), _ptr(x_im), xdtype, M, ldx, _ptr(y_re), _ptr(y_im),
+                                  ldy, algo, _ptr(positions), head_dim, float(base), _stream(stream)),
+           "fairy_cgemm_rope")

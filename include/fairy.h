@@ -206,6 +206,26 @@ fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x
                          float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Rotary position encoding fused into the output ---------------------------
+ * [iFairy press article §三 and iFairy talk §2.1.3: on the complex plane the
+ * rotary position encoding is one complex multiplication per output]
+ * Same as fairy_cgemv / fairy_cgemm (no raw accumulators), then every output
+ *   y[b][r] <- y[b][r] * exp(i * positions[b] * theta_j),
+ *   j = r % head_dim,  theta_j = base^(-j / head_dim),
+ * i.e. the rotate-half real RoPE of a real head of 2*head_dim dimensions
+ * whose dimension pairs (j, j + head_dim) are the complex dimension j.
+ * Angles and the rotation are evaluated in fp64 and rounded once to fp32.
+ *   positions : device int32 [batch] (or [M]), 4-byte aligned
+ *   head_dim  : complex dimensions per head, >= 1;  base : finite, > 0. */
+fairy_status fairy_cgemv_rope(const fairy_clinear* L, const void* x_re, const void* x_im,
+                              int32_t xdtype, int32_t batch, int64_t ldx,
+                              float* y_re, float* y_im, int64_t ldy,
+                              const int32_t* positions, int32_t head_dim, float base, void* stream);
+fairy_status fairy_cgemm_rope(const fairy_clinear* L, const void* x_re, const void* x_im,
+                              int32_t xdtype, int64_t M, int64_t ldx,
+                              float* y_re, float* y_im, int64_t ldy, int32_t algo,
+                              const int32_t* positions, int32_t head_dim, float base, void* stream);
+
 /* ---- Whole-layer conversion on the device ----------------------------------
  * [Fairy2i article §2.1 (widely-linear split), §3.1-§3.2 (PhaseQuant codes and
  * axis scales), §4.1 (recursive residual stages)]: the steps above chained on

@@ -149,3 +149,21 @@ def test_cattention_validation():
     assert call(dt=F.FAIRY_I8) == F.FAIRY_ERR_UNSUPPORTED
     assert call(d=48) == F.FAIRY_ERR_UNSUPPORTED
     assert call(d=256) == F.FAIRY_ERR_UNSUPPORTED
+
+
+def test_rope_validation():
+    import ctypes
+    L = F.make_clinear(64, 64, 2, 1, A, A)
+    f = F.lib().fairy_cgemv_rope
+    g = F.lib().fairy_cgemm_rope
+    r = ctypes.byref(L)
+    assert f(r, A, A, F.FAIRY_BF16, 1, 64, A, A, 64, None, 64, 10000.0, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(r, A, A, F.FAIRY_BF16, 1, 64, A, A, 64, A + 2, 64, 10000.0, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(r, A, A, F.FAIRY_BF16, 1, 64, A, A, 64, A, 0, 10000.0, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(r, A, A, F.FAIRY_BF16, 1, 64, A, A, 64, A, 64, 0.0, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(r, A, A, F.FAIRY_BF16, 1, 64, A, A, 64, A, 64, float("inf"), None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(r, A, A, F.FAIRY_BF16, 65, 64, A, A, 64, A, 64, 10000.0, None) == F.FAIRY_ERR_INVALID_ARG
+    assert g(r, A, A, F.FAIRY_BF16, 0, 64, A, A, 64, F.FAIRY_ALGO_AUTO, A, 64, 10000.0, None) == F.FAIRY_ERR_INVALID_ARG
+    assert g(r, A, A, F.FAIRY_BF16, 8, 64, A, A, 64, 9, A, 64, 10000.0, None) == F.FAIRY_ERR_INVALID_ARG
+    assert g(r, A, A, F.FAIRY_F32, 8, 64, A, A, 64, F.FAIRY_ALGO_MFMA, A, 64, 10000.0, None) == F.FAIRY_ERR_UNSUPPORTED
+    assert g(r, A, A, F.FAIRY_BF16, 8, 64, A, A, 64, F.FAIRY_ALGO_AUTO, None, 64, 10000.0, None) == F.FAIRY_ERR_INVALID_ARG
