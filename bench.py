@@ -42,7 +42,7 @@ GEMV_KERNEL = "k_cgemv_lp<bf16,P=4,BCH=1> (one row per wave, lane-fixed planes)"
 # HBM bytes per launch of GEMV_KERNEL on this workload, from the FETCH_SIZE and
 # WRITE_SIZE counters scaled by a plain copy's (profiles/gemv_lp_bf16_2048x2048_S2_B1.md);
 # None whenever the kernel has changed since those counters were taken
-GEMV_TRAFFIC_BYTES = None
+GEMV_TRAFFIC_BYTES = 4368180
 POOL_BYTES = 512 << 20
 
 
@@ -209,6 +209,9 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="only time the M=2048 prefill GEMM on the 2048x2048 S=2 layer (bf16 and int8, "
                          "matrix cores), e.g. under a profiler")
+    ap.add_argument("--attention", action="store_true",
+                    help="only time the complex attention at 32 heads x 2048 tokens, d 64 (causal and full), "
+                         "e.g. under a profiler")
     ap.add_argument("--calib", action="store_true",
                     help="only measure the ceilings: a plain 256 MiB copy (the byte-counter calibration "
                          "kernel), 4 MiB and 32 MiB copy launches and tiny launches in HIP graphs")
@@ -223,6 +226,12 @@ def main():
     torch, F, synth = bn.torch, bn.F, bn.synth
     if args.calib:
         print(json.dumps(calibrate(bn)), flush=True)
+        return
+    if args.attention:
+        out = {f"cattention_32x2048_d64_{'causal' if c else 'full'}": bn.attention_rate(32, 2048, 2048, 64, c,
+                                                                                      iters=args.steps)
+               for c in (1, 0)}
+        print(json.dumps(out), flush=True)
         return
     if args.prefill:
         L = bn.widely_linear_layer(4096, 4096, 2, seed=200)
