@@ -139,6 +139,21 @@ class Bench:
         ms, _ = self.graph_time(f, steps)
         return ms
 
+    def lut_rate(self, L, descs, steps=200, seed=202):
+        """Table-lookup GEMV, batch 1, bf16 activations, over the weight pool."""
+        torch, F = self.torch, self.F
+        n, m = L["n"], L["m"]
+        xr, xi = self.synth.bf16_gaussian((1, m), seed)
+        xr, xi = self.dev(xr), self.dev(xi)
+        yr = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        yi = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        wsb = F.fairy_cgemv_lut_workspace_bytes(descs[0])
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+        f = lambda i: F.fairy_cgemv_lut(descs[i % len(descs)], xr, xi, F.FAIRY_BF16, yr, yi, ws, wsb)
+        f(0)
+        ms, _ = self.graph_time(f, steps)
+        return ms
+
     def attention_rate(self, h, sq, sk, d, causal, iters=10, seed=205):
         torch, F = self.torch, self.F
         bufs = []
@@ -186,6 +201,12 @@ def attention_entry(ms, h, sq, sk, d, causal):
             "mfma_frac": mf / t / 1e12 / MFMA_PEAK_TFLOPS["bf16"]}
 
 
+def lut_entry(ms, ms_direct, L):
+    """Table-lookup GEMV beside the direct decode on the same layer and input."""
+    return {"ms": ms, "packed_GB/s": L["packed_bytes"] / (ms * 1e-3) / 1e9,
+            "direct_ms": ms_direct, "direct_over_lut": round(ms_direct / ms, 3)}
+
+
 def gemm_entry(ms, P, n, m, M, peak=None):
     alg = 2.0 * P * n * m * M            # additions of the multiplication-free form
     mfma_ops = 8.0 * P * n * m * M       # 2 x MACs on the ternary planes (4 MACs per code per token)
@@ -212,6 +233,9 @@ def main():
     ap.add_argument("--attention", action="store_true",
                     help="only time the complex attention at 32 heads x 2048 tokens, d 64 (causal and full), "
                          "e.g. under a profiler")
+    ap.add_argument("--lut", action="store_true",
+                    help="only time the table-lookup GEMV beside the direct one, batch 1, on the 2048x2048 "
+                         "S=2 layer, e.g. under a profiler")
     ap.add_argument("--calib", action="store_true",
                     help="only measure the ceilings: a plain 256 MiB copy (the byte-counter calibration "
                          "kernel), 4 MiB and 32 MiB copy launches and tiny launches in HIP graphs")
@@ -232,6 +256,13 @@ def main():
                                                                                       iters=args.steps)
                for c in (1, 0)}
         print(json.dumps(out), flush=True)
+        return
+    if args.lut:
+        L = bn.widely_linear_layer(4096, 4096, 2, seed=200)
+        copies, descs = bn.pool(L)
+        ms_l = bn.lut_rate(L, descs, steps=args.steps)
+        ms_d = bn.gemv_rate(L, descs, 1, F.FAIRY_BF16, steps=args.steps)
+        print(json.dumps({"gemv_lut_2048x2048_bf16_B1": lut_entry(ms_l, ms_d, L)}), flush=True)
         return
     if args.prefill:
         L = bn.widely_linear_layer(4096, 4096, 2, seed=200)
@@ -348,6 +379,8 @@ def main():
                 "alg_Tadds/s": 2 * P * n * m * bb / (msb * 1e-3) / 1e12}
         ms8 = bn.gemv_rate(L, descs, 1, F.FAIRY_I8, steps=200)
         rows_out["gemv_2048x2048_i8_B1"] = {"ms": ms8, "packed_GB/s": packed_bytes / (ms8 * 1e-3) / 1e9}
+        ms1 = ms if B == 1 else bn.gemv_rate(L, descs, 1, F.FAIRY_BF16, steps=200)
+        rows_out["gemv_lut_2048x2048_bf16_B1"] = lut_entry(bn.lut_rate(L, descs), ms1, L)
         del copies, descs
         torch.cuda.empty_cache()
         # MLP shapes (gate/up: 11008x4096, down: 4096x11008)
@@ -359,6 +392,8 @@ def main():
                 msm = bn.gemv_rate(L2, d2, bb, F.FAIRY_BF16, steps=200)
                 rows_out[f"gemv_{name}_bf16_B{bb}"] = {
                     "ms": msm, "packed_GB/s": L2["packed_bytes"] / (msm * 1e-3) / 1e9}
+                if bb == 1:
+                    rows_out[f"gemv_lut_{name}_bf16_B1"] = lut_entry(bn.lut_rate(L2, d2), msm, L2)
             del c2, d2
             if name.startswith("gate"):
                 # prefill GEMM, M = 2048 tokens, on the 5504-row layer

@@ -40,7 +40,7 @@ int64_t max_m_for(int32_t xdtype)
 // the launcher's view of the layer on success.
 fairy_status check_layer_call(const fairy_clinear* L, const void* x_re, const void* x_im, int32_t xdtype,
                               int64_t rows, int64_t ldx, const float* y_re, const float* y_im, int64_t ldy,
-                              const int32_t* acc, fairy::LayerArgs* out)
+                              const int32_t* acc, fairy::LayerArgs* out, bool staged_x = true)
 {
     if (!L || !x_re || !x_im || !y_re || !y_im) return FAIRY_ERR_INVALID_ARG;
     if (L->n < 1 || L->m < 1 || L->n > kMaxDim || L->m > kMaxDim) return FAIRY_ERR_INVALID_ARG;
@@ -58,7 +58,7 @@ fairy_status check_layer_call(const fairy_clinear* L, const void* x_re, const vo
     if (ldx % 16 != 0) return FAIRY_ERR_INVALID_ARG;
     if (L->layout != FAIRY_LAYOUT_TILED64) return FAIRY_ERR_UNSUPPORTED;
     if (L->m % 16 != 0) return FAIRY_ERR_UNSUPPORTED;
-    if (L->m > max_m_for(xdtype)) return FAIRY_ERR_UNSUPPORTED;
+    if (staged_x && L->m > max_m_for(xdtype)) return FAIRY_ERR_UNSUPPORTED;
     out->packed = L->packed;
     out->scales = L->scales;
     out->n = L->n;
@@ -178,6 +178,47 @@ fairy_status fairy_cgemv(const fairy_clinear* L, const void* x_re, const void* x
     if (st != FAIRY_OK) return st;
     clear_stale_error();
     return from_hip(fairy::launch_cgemv(la, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, acc, as_stream(stream)));
+}
+
+// Layer view and block shape of a table-lookup GEMV call; false when the
+// layer is invalid or its chunk grid exceeds the launch limits.
+static bool lut_plan(const fairy_clinear* L, fairy::LayerArgs* la, fairy::LutConfig* c)
+{
+    if (!L || L->n < 1 || L->m < 1 || L->n > kMaxDim || L->m > kMaxDim) return false;
+    if (L->stages < 1 || L->stages > 8 || (L->has_conj != 0 && L->has_conj != 1)) return false;
+    la->packed = L->packed;
+    la->scales = L->scales;
+    la->n = L->n;
+    la->m = L->m;
+    la->stages = L->stages;
+    la->planes = L->stages * (1 + L->has_conj);
+    *c = fairy::cgemv_lut_config(*la);
+    const int64_t units = ((L->m + 63) / 64) * (int64_t)la->planes;
+    return (units + c->JB - 1) / c->JB <= 65535;
+}
+
+size_t fairy_cgemv_lut_workspace_bytes(const fairy_clinear* L)
+{
+    fairy::LayerArgs la;
+    fairy::LutConfig c;
+    if (!lut_plan(L, &la, &c)) return 0;
+    return fairy::cgemv_lut_workspace_bytes(la, c);
+}
+
+fairy_status fairy_cgemv_lut(const fairy_clinear* L, const void* x_re, const void* x_im, int32_t xdtype,
+                             float* y_re, float* y_im, void* workspace, size_t workspace_bytes, void* stream)
+{
+    fairy::LayerArgs la;
+    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, 1, L ? (L->m + 15) / 16 * 16 : 0, y_re, y_im, L ? L->n : 0,
+                                       nullptr, &la, false);
+    if (st != FAIRY_OK) return st;
+    if (xdtype != FAIRY_BF16 && xdtype != FAIRY_F32) return FAIRY_ERR_UNSUPPORTED;
+    fairy::LutConfig c;
+    if (!lut_plan(L, &la, &c)) return FAIRY_ERR_UNSUPPORTED;
+    const size_t need = fairy::cgemv_lut_workspace_bytes(la, c);
+    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FAIRY_ERR_WORKSPACE;
+    clear_stale_error();
+    return from_hip(fairy::launch_cgemv_lut(la, c, x_re, x_im, xdtype, y_re, y_im, workspace, as_stream(stream)));
 }
 
 size_t fairy_cgemm_workspace_bytes(const fairy_clinear* L, int64_t M, int32_t xdtype, int32_t algo)

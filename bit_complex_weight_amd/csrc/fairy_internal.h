@@ -123,6 +123,16 @@ hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, 
                         int64_t M, int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc,
                         int32_t algo, void* workspace, hipStream_t s);
 
+// table-lookup GEMV, batch 1 (fairy_gemv_lut.hip): W waves of rows and JB
+// 16-byte units per block
+struct LutConfig {
+    int W, JB;
+};
+LutConfig cgemv_lut_config(const LayerArgs& L);
+size_t cgemv_lut_workspace_bytes(const LayerArgs& L, const LutConfig& c);
+hipError_t launch_cgemv_lut(const LayerArgs& L, const LutConfig& c, const void* x_re, const void* x_im,
+                            int32_t xdtype, float* y_re, float* y_im, void* workspace, hipStream_t s);
+
 // complex attention forward (fairy_attention.hip); bf16 inputs, d in {32, 64, 128}
 hipError_t launch_cattention(const void* q_re, const void* q_im, const void* k_re, const void* k_im,
                              const void* v_re, const void* v_im, int32_t heads, int64_t sq, int64_t sk, int32_t d,

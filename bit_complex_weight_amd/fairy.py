@@ -127,6 +127,10 @@ def lib() -> ctypes.CDLL:
         L.fairy_cgemm_rope.argtypes = [ctypes.POINTER(fairy_clinear), _p, _p, _i32, _i64, _i64, _p, _p, _i64, _i32, _p,
                                        _i32, ctypes.c_float, _p]
         L.fairy_cgemm_rope.restype = _i32
+        L.fairy_cgemv_lut_workspace_bytes.argtypes = [ctypes.POINTER(fairy_clinear)]
+        L.fairy_cgemv_lut_workspace_bytes.restype = _sz
+        L.fairy_cgemv_lut.argtypes = [ctypes.POINTER(fairy_clinear), _p, _p, _i32, _p, _p, _p, _sz, _p]
+        L.fairy_cgemv_lut.restype = _i32
         _lib = L
     return _lib
 
@@ -290,3 +294,12 @@ def fairy_cgemm_rope(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, algo, posit
     _check(lib().fairy_cgemm_rope(ctypes.byref(L), _ptr(x_re), _ptr(x_im), xdtype, M, ldx, _ptr(y_re), _ptr(y_im),
                                   ldy, algo, _ptr(positions), head_dim, float(base), _stream(stream)),
            "fairy_cgemm_rope")
+
+
+def fairy_cgemv_lut_workspace_bytes(L) -> int:
+    return lib().fairy_cgemv_lut_workspace_bytes(ctypes.byref(L))
+
+
+def fairy_cgemv_lut(L, x_re, x_im, xdtype, y_re, y_im, workspace=None, workspace_bytes=0, stream=None):
+    _check(lib().fairy_cgemv_lut(ctypes.byref(L), _ptr(x_re), _ptr(x_im), xdtype, _ptr(y_re), _ptr(y_im),
+                                 _ptr(workspace), workspace_bytes, _stream(stream)), "fairy_cgemv_lut")

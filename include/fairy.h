@@ -194,6 +194,28 @@ fairy_status fairy_cgemv(const fairy_clinear* L, const void* x_re, const void* x
                          float* y_re, float* y_im, int64_t ldy, int32_t* acc,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Table-lookup GEMV (batch 1) ----------------------------------------------
+ * [iFairy talk §2.3.2: table-lookup inference precomputes the results of the
+ * 16 input combinations of a pair of codes]  Same result as fairy_cgemv with
+ * batch = 1, computed another way: for every pair of same-parity columns held
+ * in one 4-bit field of a TILED64 word and every plane, a 16-entry table of
+ * (y_re, y_im) contributions is built from x and the plane's scales, and each
+ * pair of codes costs one table read and two adds.  Kept as a measured
+ * alternative to the direct bit decode of fairy_cgemv.
+ *   x_re, x_im : [m] of xdtype (F32 or BF16; I8 is UNSUPPORTED), 16-byte aligned.
+ *   y_re, y_im : [n] fp32, overwritten.
+ *   workspace  : device, 16-byte aligned, at least
+ *                fairy_cgemv_lut_workspace_bytes(L) bytes (partial sums of
+ *                the column chunks); may be NULL when that is 0.
+ * The layer must be TILED64 with m % 16 == 0 (no limit on m from LDS).
+ * Float outputs are within 1e-5 relative L2 of the exact result; the chunk
+ * partials are added in a fixed order, so repeated calls are bitwise equal.
+ * fairy_cgemv_lut_workspace_bytes returns 0 for an invalid layer as well. */
+size_t fairy_cgemv_lut_workspace_bytes(const fairy_clinear* L);
+fairy_status fairy_cgemv_lut(const fairy_clinear* L, const void* x_re, const void* x_im,
+                             int32_t xdtype, float* y_re, float* y_im,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes fairy_cgemm needs. */
 size_t fairy_cgemm_workspace_bytes(const fairy_clinear* L, int64_t M, int32_t xdtype, int32_t algo);
 

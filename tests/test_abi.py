@@ -175,6 +175,32 @@ def test_cgemm_validation():
     assert f(*args(dt=F.FAIRY_F32, algo=F.FAIRY_ALGO_MFMA)) == F.FAIRY_ERR_UNSUPPORTED
 
 
+def test_cgemv_lut_validation():
+    f, ws = L_.fairy_cgemv_lut, L_.fairy_cgemv_lut_workspace_bytes
+    big = layer(n=2048, m=2048)
+    need = ws(ctypes.byref(big))
+    assert need > 0 and need % (8 * 2048) == 0   # fp32 (re, im) partial rows per column chunk
+    assert ws(ctypes.byref(layer(m=16, stages=1, has_conj=0))) == 0   # one 16-byte unit per row: one chunk
+    assert ws(ctypes.byref(layer(n=0))) == 0
+    assert ws(None) == 0
+
+    def call(Lr, dt=F.FAIRY_BF16, xr=A, w=None, wb=0):
+        return f(ctypes.byref(Lr) if Lr is not None else None, xr, A, dt, A, A, w, wb, None)
+
+    assert call(None) == F.FAIRY_ERR_INVALID_ARG
+    assert call(layer(n=0)) == F.FAIRY_ERR_INVALID_ARG
+    assert call(layer(stages=9)) == F.FAIRY_ERR_INVALID_ARG
+    assert call(layer(packed=0)) == F.FAIRY_ERR_INVALID_ARG
+    assert call(layer(), xr=A + 2) == F.FAIRY_ERR_INVALID_ARG
+    assert call(layer(), dt=7) == F.FAIRY_ERR_INVALID_ARG
+    assert call(layer(), dt=F.FAIRY_I8) == F.FAIRY_ERR_UNSUPPORTED
+    assert call(layer(m=40)) == F.FAIRY_ERR_UNSUPPORTED
+    assert call(layer(layout=F.FAIRY_LAYOUT_ROW16)) == F.FAIRY_ERR_UNSUPPORTED
+    assert call(big) == F.FAIRY_ERR_WORKSPACE
+    assert call(big, w=A, wb=need - 1) == F.FAIRY_ERR_WORKSPACE
+    assert call(big, w=A + 4, wb=need) == F.FAIRY_ERR_WORKSPACE
+
+
 def test_python_binding_rejects_host_buffers():
     import numpy as np
     with pytest.raises(TypeError):
