@@ -31,9 +31,18 @@ FLAGS = [
 ]
 
 
+# Per-source code-generation options.  The attention kernel runs softmax
+# arithmetic on its MFMA results every key chunk; with the accumulators in
+# ordinary VGPRs (the MFMA "VGPR form") no accumulator-register moves are
+# needed around that arithmetic.
+SOURCE_FLAGS = {
+    "fairy_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -45,17 +45,24 @@ struct Args {
     int32_t causal;
 };
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+
+// (x0, x1) -> the packed bf16 pair nearest to them (ties to even), one
+// v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t bf16x2_rne(float x0, float x1)
 {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // finite inputs only
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2_t{x0, x1}), bf16x2_t));
 }
 
 template <int D>
 struct Geometry {
     static constexpr int D2 = 2 * D;              // length of the concatenated [re | im] vector
     static constexpr int kRowK = D2 * 2 + 16;     // bytes per staged key row (+ pad: conflict-free reads)
-    static constexpr int kRowV = kKeys * 2 + 16;  // bytes per staged V^T row
+    // bytes per staged V^T row: 8 more than the 128 of a row's keys, so the
+    // 16 rows that one pass of an 8-byte read touches start on distinct
+    // bank pairs
+    static constexpr int kRowV = kKeys * 2 + 8;
     static constexpr int kBytesK = kKeys * kRowK;
     static constexpr int kBytesV = 2 * D * kRowV;
 };
@@ -110,30 +117,37 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
     constexpr int VP = (VN + kThreads - 1) / kThreads;
     static_assert(KP * kThreads == kKeys * (D2 / 8), "staging split");
     uint4 kreg[KP], vreg[VP][4];
-    auto load_chunk = [&](int64_t c0) {
+    // guard = false: the chunk lies inside the keys (every chunk but a
+    // ragged last one), so its loads need no bounds checks
+    auto load_chunk_g = [&](int64_t c0, bool guard) {
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const int p = i * kThreads + threadIdx.x;
             const int key = p / (D2 / 8), dim0 = 8 * (p % (D2 / 8));
             const int64_t kj = c0 + key;
-            kreg[i] = (kj < a.sk) ? *reinterpret_cast<const uint4*>((dim0 < D ? a.k_re : a.k_im) +
-                                                                   (h * a.sk + kj) * D + (dim0 % D))
-                                  : make_uint4(0, 0, 0, 0);
+            const uint4* src = reinterpret_cast<const uint4*>((dim0 < D ? a.k_re : a.k_im) + (h * a.sk + kj) * D +
+                                                              (dim0 % D));
+            kreg[i] = (!guard || kj < a.sk) ? *src : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < VP; ++i) {
             const int p = i * kThreads + threadIdx.x;
             const int comp = p / ((kKeys / 4) * (D / 8));
             const int rem = p - comp * (kKeys / 4) * (D / 8);
-            const int key0 = 4 * (rem / (D / 8)), d0 = 8 * (rem % (D / 8));
+            const int key0 = 4 * (rem % (kKeys / 4)), d0 = 8 * (rem / (kKeys / 4));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t kj = c0 + key0 + r;
-                vreg[i][r] = (p < VN && kj < a.sk) ? *reinterpret_cast<const uint4*>((comp ? a.v_im : a.v_re) +
-                                                                          (h * a.sk + kj) * D + d0)
-                                         : make_uint4(0, 0, 0, 0);
+                const uint4* src = reinterpret_cast<const uint4*>((comp ? a.v_im : a.v_re) + (h * a.sk + kj) * D + d0);
+                vreg[i][r] = (p < VN && (!guard || kj < a.sk)) ? *src : make_uint4(0, 0, 0, 0);
             }
         }
+    };
+    auto load_chunk = [&](int64_t c0) {
+        if (c0 + kKeys <= a.sk)
+            load_chunk_g(c0, false);
+        else
+            load_chunk_g(c0, true);
     };
     auto store_chunk = [&]() {
 #pragma unroll
@@ -149,7 +163,8 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
             if (p >= VN) continue;
             const int comp = p / ((kKeys / 4) * (D / 8));
             const int rem = p - comp * (kKeys / 4) * (D / 8);
-            const int key0 = 4 * (rem / (D / 8)), d0 = 8 * (rem % (D / 8));
+            // 16 consecutive threads write one V^T row's 128 bytes
+            const int key0 = 4 * (rem % (kKeys / 4)), d0 = 8 * (rem / (kKeys / 4));
             const uint32_t w[4][4] = {{vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w},
                                       {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w},
                                       {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w},
@@ -182,17 +197,33 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
                 st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t], st[kt], 0, 0, 0);
             }
         }
+        // Masking is needed only where the chunk runs past the keys or,
+        // causal, past the diagonal of the wave's first query (wave-uniform).
+        const int64_t q_first = qb * kQBlock + wave * 16;
+        const bool edge = k0 + kKeys > a.sk || (a.causal && k0 + kKeys - 1 > q_first + diag);
         float s[4][4];
         float mx = -INFINITY;
+        if (edge) {
+            // keys k0 + r with r < lim are visible to this lane's query
+            int64_t lim64 = a.sk - k0;
+            if (a.causal && qi + diag + 1 - k0 < lim64) lim64 = qi + diag + 1 - k0;
+            const int lim = (int)(lim64 < 0 ? 0 : lim64 > kKeys ? kKeys : lim64);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t kj = k0 + 16 * kt + 4 * g + v;
-                const bool masked = kj >= a.sk || (a.causal && kj > qi + diag);
-                s[kt][v] = masked ? -INFINITY : scale2 * st[kt][v];
-                mx = fmaxf(mx, s[kt][v]);
-            }
+                for (int v = 0; v < 4; ++v) {
+                    s[kt][v] = (16 * kt + 4 * g + v < lim) ? scale2 * st[kt][v] : -INFINITY;
+                    mx = fmaxf(mx, s[kt][v]);
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    s[kt][v] = scale2 * st[kt][v];
+                    mx = fmaxf(mx, s[kt][v]);
+                }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         // key k0 (<= qi + diag) is unmasked in the first chunk, so m_new is finite
@@ -209,11 +240,15 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
         ls += __shfl_xor(ls, 16);
         ls += __shfl_xor(ls, 32);
         l_run = l_run * corr + ls;
+        // the output is rescaled only when some query's maximum moved
+        // (corr == 1 exactly otherwise)
+        if (__ballot(m_new != m_run)) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int t = 0; t < DT; ++t) o[c][t] *= corr;
+        }
         m_run = m_new;
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int t = 0; t < DT; ++t) o[c][t] *= corr;
 
         // O^T += V^T P^T, two K-steps of 32 keys, P as bf16 hi + lo
 #pragma unroll
@@ -223,11 +258,8 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
             for (int e = 0; e < 4; ++e) {
                 const float x0 = (e < 2) ? p[2 * ks][2 * e] : p[2 * ks + 1][2 * e - 4];
                 const float x1 = (e < 2) ? p[2 * ks][2 * e + 1] : p[2 * ks + 1][2 * e - 3];
-                const uint32_t h0 = bf16_bits_rne(x0), h1 = bf16_bits_rne(x1);
-                const uint32_t l0 = bf16_bits_rne(x0 - __uint_as_float(h0 << 16));
-                const uint32_t l1 = bf16_bits_rne(x1 - __uint_as_float(h1 << 16));
-                hi[e] = h0 | (h1 << 16);
-                lo[e] = l0 | (l1 << 16);
+                hi[e] = bf16x2_rne(x0, x1);
+                lo[e] = bf16x2_rne(x0 - __uint_as_float(hi[e] << 16), x1 - __uint_as_float(hi[e] & 0xFFFF0000u));
             }
             const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
             const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
