@@ -438,7 +438,7 @@ def main():
             oracle.cgemv_dense(oc, osc, S, True, xr, xi)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or reps >= 2000:
+            if el >= args.cpu_seconds or reps >= 100000:
                 break
         result["cpu_baseline"] = {
             "value": round(packed_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
@@ -490,6 +490,17 @@ def full_layer_sweep(bn):
     for S in (1, 2, 3):
         layers = {name: bn.widely_linear_layer(rr, cc, S, 500 + 10 * S + i)
                   for i, (name, (rr, cc)) in enumerate(proj.items())}
+        # PhaseQuant of every projection's U and W (rewrites the same codes
+        # and scales the layer was packed from)
+        pq = {}
+        for name, L in layers.items():
+            def quant(i, L=L):
+                for k in (0, 2):
+                    F.fairy_phasequant(L["planes"][k], L["planes"][k + 1], L["count"], S, L["codes"][k // 2 * S],
+                                       L["scales"][k // 2 * S], None, None, L["ws"], L["wsb"])
+            pq[name] = bn.ev_time(quant, 3)
+        out[f"phasequant_layer_S{S}"] = {"ms_total": sum(pq.values()), "per_proj_ms": pq}
+        log(f"sweep S={S}: PhaseQuant of U and W over the 7 projections {sum(pq.values()):.3f} ms")
         for B in (1, 4, 16, 64):
             tot_ms, tot_bytes, per = 0.0, 0, {}
             for name, L in layers.items():

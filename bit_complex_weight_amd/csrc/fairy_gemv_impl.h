@@ -228,13 +228,17 @@ __global__ __launch_bounds__(kThreads) void k_cgemv_units(GemvArgs a)
     const int col_bytes = x_bytes_per_col(XT, a.m64);
     const int plane_bytes = col_bytes / 2;
 
-    for (int b0 = 0; b0 < a.B; b0 += BCH) {
+    // blockIdx.y picks the first chunk of BCH batch columns; chunks run side
+    // by side on the grid (a block loops only if the grid has fewer chunks)
+    bool first = true;
+    for (int b0 = blockIdx.y * BCH; b0 < a.B; b0 += gridDim.y * BCH) {
         const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
-        if (b0) {
+        if (!first) {
             __syncthreads();
 #pragma unroll
             for (int k = 0; k < UB; ++k) cw[k] = (k < nmine) ? wrow[lr + k * TROW] : make_uint4(0, 0, 0, 0);
         }
+        first = false;
         stage_x<XT>(a, b0, nb, xs);
         __syncthreads();
 
@@ -286,8 +290,10 @@ __global__ __launch_bounds__(kThreads) void k_cgemv_units(GemvArgs a)
 
 
 // ---------------------------------------------------------------------------
-// Float paths, plane count P dividing 64 and rows of >= 64 units: one row per
-// wave, lane l owns plane l % P and groups l/P + k*(64/P).
+// Float paths, rows of >= 64 units: one row per wave.  The first
+// NL = (64/P)*P lanes are active (all 64 when P divides 64; 60 for P = 6),
+// lane l owns plane l % P and groups l/P + k*(64/P), so each step of the wave
+// reads NL consecutive units.
 // ---------------------------------------------------------------------------
 constexpr int kThreadsLp = 512;
 
@@ -296,8 +302,9 @@ constexpr int kThreadsLp = 512;
 template <int XT, int P, int BCH>
 __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
 {
-    static_assert(64 % P == 0, "plane count must divide the wave");
+    static_assert(P >= 1 && P <= 64, "plane count");
     constexpr int GS = 64 / P;  // groups one step of the wave covers
+    constexpr int NL = GS * P;  // active lanes
     constexpr int esize = (XT == FAIRY_BF16) ? 2 : 4;
     constexpr int per_elems = 16 / esize;
     extern __shared__ __align__(16) uint8_t lds[];
@@ -305,14 +312,17 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
     const int row = blockIdx.x * (kThreadsLp / 64) + (threadIdx.x >> 6);
     const bool row_ok = row < a.n;
     const int p = lane % P, gl = lane / P;
+    // an idle lane must accumulate nothing (a zero code word decodes to +1)
+    const bool active = NL == 64 || lane < NL;
     const int G = a.G;
     const int b0 = blockIdx.y * BCH;
     const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
-    // unit (g, p) of the row is at g*P + p = lane + 64k for g = gl + GS*k
+    // unit (g, p) of the row is at g*P + p = lane + NL*k for g = gl + GS*k
     const uint4* wl = reinterpret_cast<const uint4*>(a.packed) + ((int64_t)(row_ok ? row : 0) * G * P + lane);
     uint4 cur[2], nxt[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) cur[u] = (row_ok && gl + u * GS < G) ? wl[64 * u] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 2; ++u)
+        cur[u] = (row_ok && active && gl + u * GS < G) ? wl[NL * u] : make_uint4(0, 0, 0, 0);
     // decoded weights are +-2: half-scales; W planes multiply conj(x)
     const float hr = 0.5f * a.scales[2 * p], hi = 0.5f * a.scales[2 * p + 1];
     const float sg = (p < a.S) ? 1.0f : -1.0f;
@@ -342,11 +352,12 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
         const int gn = g0 + 2 * GS;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            nxt[u] = (row_ok && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + 64 * u] : make_uint4(0, 0, 0, 0);
+            nxt[u] = (row_ok && active && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + NL * u]
+                                                             : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int g = g0 + u * GS;
-            if (g < G) unit_accumulate<XT, BCH>(cur[u], 64 * g, lds, col_bytes, pbytes, nb, A);
+            if (active && g < G) unit_accumulate<XT, BCH>(cur[u], 64 * g, lds, col_bytes, pbytes, nb, A);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) cur[u] = nxt[u];
@@ -500,7 +511,10 @@ int pick_bch(int xdtype, int B, int m64);
 template <int XT, int TROW, int BCH>
 hipError_t launch_units_t(const GemvArgs& a, hipStream_t s)
 {
-    const dim3 grid((a.n + (kThreads / TROW) - 1) / (kThreads / TROW));
+    // batch chunks on grid.y, at most 65535 (the kernel loops over the rest:
+    // the token rows of the VALU prefill path take this launcher too)
+    const int64_t chunks = ((int64_t)a.B + BCH - 1) / BCH;
+    const dim3 grid((a.n + (kThreads / TROW) - 1) / (kThreads / TROW), (unsigned)(chunks < 65535 ? chunks : 65535));
     const size_t lds = kScaleBytes + (size_t)x_bytes_per_col(XT, a.m64) * BCH;
     hipLaunchKernelGGL((k_cgemv_units<XT, TROW, BCH, 2>), grid, dim3(kThreads), lds, s, a);
     return hipGetLastError();
@@ -550,7 +564,9 @@ hipError_t launch_float(const GemvArgs& a, hipStream_t s)
         switch (a.P) {
         case 1: return launch_lp_bch<XT, 1>(a, bl, s);
         case 2: return launch_lp_bch<XT, 2>(a, bl, s);
+        case 3: return launch_lp_bch<XT, 3>(a, bl, s);
         case 4: return launch_lp_bch<XT, 4>(a, bl, s);
+        case 6: return launch_lp_bch<XT, 6>(a, bl, s);
         case 8: return launch_lp_bch<XT, 8>(a, bl, s);
         case 16: return launch_lp_bch<XT, 16>(a, bl, s);
         default: break;

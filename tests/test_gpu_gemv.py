@@ -72,6 +72,11 @@ CASES = [
     (1, True, 33, 2064, 5),      # P = 2
     (4, True, 19, 528, 6),       # P = 8
     (8, True, 5, 272, 2),        # P = 16
+    # one row per wave with idle lanes (P does not divide 64: 60 or 63 lanes)
+    (3, True, 21, 704, 3),       # P = 6, 11 groups: a second, partial step
+    (3, False, 17, 1360, 2),     # P = 3, ragged last group
+    (3, True, 40, 2048, 16),     # P = 6, the 2048-column shape
+    (3, True, 9, 1024, 64),      # P = 6, batch 64
 ]
 
 
