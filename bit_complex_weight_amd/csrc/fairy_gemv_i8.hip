@@ -6,6 +6,138 @@ namespace fairy {
 namespace gemv {
 namespace {
 
+// ---------------------------------------------------------------------------
+// One row per wave for rows of >= 64 units and a power-of-two plane count:
+// lane l owns plane l % P and groups l/P + k*(64/P), as on the float path.
+// A lane's four int32 sums cover its own plane, so a butterfly over the
+// lanes of the same plane (xor distances P..32) gives each of them that
+// plane's exact totals (the raw accumulators), and a second one over the
+// distances below P adds the scaled planes in float.
+// ---------------------------------------------------------------------------
+template <int P>
+__device__ __forceinline__ int plane_total(int v)
+{
+    if (P <= 1) v += dpp_xor1(v);
+    if (P <= 2) v += dpp_xor2(v);
+    if (P <= 4) v += swz_xor4(v);
+    if (P <= 8) v += swz_xor8(v);
+    if (P <= 16) v += swz_xor16(v);
+    if (P <= 32) v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int BCH>
+__device__ __forceinline__ void unit_i8(const uint4 cw, int g, const uint8_t* xs, int pbytes, int (&A)[4][BCH])
+{
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        uint32_t re[4], im[4];
+        ternary_bytes(words[u], re, im);
+        const int off = x_col_off(FAIRY_I8, 64 * g + 16 * u);
+#pragma unroll
+        for (int b = 0; b < BCH; ++b) {
+            const uint8_t* xb = xs + (size_t)b * 2 * pbytes + off;
+            const uint4 xr4 = *reinterpret_cast<const uint4*>(xb);
+            const uint4 xi4 = *reinterpret_cast<const uint4*>(xb + pbytes);
+            const uint32_t xr[4] = {xr4.x, xr4.y, xr4.z, xr4.w};
+            const uint32_t xi[4] = {xi4.x, xi4.y, xi4.z, xi4.w};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                A[0][b] = __builtin_amdgcn_sdot4((int)re[s], (int)xr[s], A[0][b], false);
+                A[1][b] = __builtin_amdgcn_sdot4((int)im[s], (int)xi[s], A[1][b], false);
+                A[2][b] = __builtin_amdgcn_sdot4((int)re[s], (int)xi[s], A[2][b], false);
+                A[3][b] = __builtin_amdgcn_sdot4((int)im[s], (int)xr[s], A[3][b], false);
+            }
+        }
+    }
+}
+
+template <int P, int BCH>
+__global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp_i8(GemvArgs a)
+{
+    static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "power-of-two plane count");
+    constexpr int GS = 64 / P;  // groups one step of the wave covers
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * (kThreadsLp / 64) + (threadIdx.x >> 6);
+    const bool row_ok = row < a.n;
+    const int p = lane % P, gl = lane / P;
+    const int G = a.G;
+    const int b0 = blockIdx.y * BCH;
+    const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
+    // unit (g, p) of the row is at g*P + p = lane + 64k for g = gl + GS*k
+    const uint4* wl = reinterpret_cast<const uint4*>(a.packed) + ((int64_t)(row_ok ? row : 0) * G * P + lane);
+    uint4 cur[2], nxt[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) cur[u] = (row_ok && gl + u * GS < G) ? wl[64 * u] : make_uint4(0, 0, 0, 0);
+    stage_x<FAIRY_I8>(a, b0, nb, lds);
+    __syncthreads();
+    const int pbytes = x_plane_bytes(FAIRY_I8, a.m64);
+
+    int A[4][BCH];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < BCH; ++b) A[q][b] = 0;
+    for (int g0 = gl; g0 < G; g0 += 2 * GS) {
+        // the next two units are in flight while these two are summed
+        const int gn = g0 + 2 * GS;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            nxt[u] = (row_ok && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + 64 * u] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int g = g0 + u * GS;
+            if (g < G) unit_i8<BCH>(cur[u], g, lds, pbytes, A);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) cur[u] = nxt[u];
+    }
+    const float s_re = a.scales[2 * p], s_im = a.scales[2 * p + 1];
+    const float sg = (p < a.S) ? 1.0f : -1.0f;  // W planes multiply conj(x)
+#pragma unroll
+    for (int b = 0; b < BCH; ++b) {
+        int t[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = plane_total<P>(A[q][b]);
+        if (a.acc && row_ok && b < nb && lane < P) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a.acc[(((int64_t)p * 4 + q) * a.B + (b0 + b)) * a.n + row] = t[q];
+        }
+        float vr = s_re * (float)t[0] - sg * (s_im * (float)t[1]);
+        float vi = sg * (s_re * (float)t[2]) + s_im * (float)t[3];
+        if constexpr (P > 1) {
+            vr = group_sum<P>(vr);
+            vi = group_sum<P>(vi);
+        }
+        if (lane == 0 && row_ok && b < nb) {
+            rope_apply(a, row, b0 + b, vr, vi);
+            a.y_re[(int64_t)(b0 + b) * a.ldy + row] = vr;
+            a.y_im[(int64_t)(b0 + b) * a.ldy + row] = vi;
+        }
+    }
+}
+
+template <int P, int BCH>
+hipError_t launch_lp_i8_t(const GemvArgs& a, hipStream_t s)
+{
+    const dim3 grid((a.n + (kThreadsLp / 64) - 1) / (kThreadsLp / 64), (a.B + BCH - 1) / BCH);
+    const size_t lds = (size_t)x_bytes_per_col(FAIRY_I8, a.m64) * BCH;
+    hipLaunchKernelGGL((k_cgemv_lp_i8<P, BCH>), grid, dim3(kThreadsLp), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_lp_i8(const GemvArgs& a, hipStream_t s)
+{
+    switch (pick_bch_lp(FAIRY_I8, a.B, a.m64)) {
+    case 4: return launch_lp_i8_t<P, 4>(a, s);
+    case 2: return launch_lp_i8_t<P, 2>(a, s);
+    default: return launch_lp_i8_t<P, 1>(a, s);
+    }
+}
+
 template <int PMAX, int TROW>
 hipError_t launch_i8_t(const GemvArgs& a, int bch, hipStream_t s)
 {
@@ -31,6 +163,16 @@ hipError_t launch_i8_p(const GemvArgs& a, int bch, hipStream_t s)
 
 hipError_t launch_i8(const GemvArgs& a, hipStream_t s)
 {
+    if (a.G * a.P >= 64 && a.B <= 64) {
+        switch (a.P) {
+        case 1: return launch_lp_i8<1>(a, s);
+        case 2: return launch_lp_i8<2>(a, s);
+        case 4: return launch_lp_i8<4>(a, s);
+        case 8: return launch_lp_i8<8>(a, s);
+        case 16: return launch_lp_i8<16>(a, s);
+        default: break;
+        }
+    }
     const int bch = pick_bch(FAIRY_I8, a.B, a.m64);
     if (a.G >= 24) return launch_i8_p<32>(a, bch, s);
     return launch_i8_p<8>(a, bch, s);
