@@ -48,7 +48,7 @@ struct LutArgs {
     float* out_re;  // y (one chunk) or the chunk partials [chunk][n]
     float* out_im;
     int64_t n;
-    int32_t m, G, P, S, JB, UR;  // UR = G * P units per row
+    int32_t m, P, S, JB, UR;  // UR = 16-byte units per row (groups x planes)
 };
 
 template <int XT>
@@ -215,11 +215,10 @@ hipError_t launch_cgemv_lut(const LayerArgs& L, const LutConfig& c, const void* 
     a.x_im = x_im;
     a.n = L.n;
     a.m = (int32_t)L.m;
-    a.G = (int32_t)((L.m + 63) / 64);
     a.P = L.planes;
     a.S = L.stages;
     a.JB = c.JB;
-    a.UR = a.G * a.P;
+    a.UR = (int32_t)((L.m + 63) / 64) * a.P;
     const int64_t chunks = (a.UR + c.JB - 1) / c.JB;
     if (chunks > 65535) return hipErrorInvalidValue;
     float* part = static_cast<float*>(workspace);
