@@ -9,16 +9,17 @@
 //
 // One pass, online softmax (FlashAttention style).  A block is 4 waves over
 // 64 queries of one head; each wave owns 16 queries and walks the keys in
-// chunks of 64 staged in LDS (keys as [key][re | im], values transposed to
-// [re/im][d][key]).
+// chunks of 64 staged in LDS (keys as [key][re | im], values as
+// [re/im][key][d], both copied as they are in memory).
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
 //    K-dim = 2d): lane l then holds query l % 16 and keys 4(l/16) + v of each
 //    16-key tile, so the running maximum and sum of a query live in the four
 //    lanes l % 16 and combine with two xor-shuffles.
 //  * The weights P^T are the B operand of O^T = V^T P^T directly: in K-step s
 //    of a chunk, lane group g = l/16 supplies keys 32s + 4g + 0..3 and
-//    32s + 16 + 4g + 0..3, and the A fragments of V^T are read from LDS in
-//    the same key order.  P is split into bf16 hi + lo (two MFMAs), so the
+//    32s + 16 + 4g + 0..3, and the A fragments of V^T are read from the
+//    natural-order values in the same key order by LDS transpose reads
+//    (ds_read_b64_tr_b16, two per fragment).  P is split into bf16 hi + lo (two MFMAs), so the
 //    weights keep ~2^-17 relative precision instead of bf16's 2^-9; the
 //    scores are exact products of the bf16 inputs summed in fp32.
 //  * O^T accumulates in fp32: lane l holds query l % 16 and four consecutive
@@ -55,16 +56,27 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float x0, float x1)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2_t{x0, x1}), bf16x2_t));
 }
 
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives as element
+// k the 16-bit element i % 4 of the 8 bytes that lane 4k + i/4 addresses
+__device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p)
+{
+    const shortx4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) shortx4_t*)(const_cast<uint8_t*>(p)));
+    return __builtin_bit_cast(uint2, v);
+}
+
 template <int D>
 struct Geometry {
     static constexpr int D2 = 2 * D;              // length of the concatenated [re | im] vector
     static constexpr int kRowK = D2 * 2 + 16;     // bytes per staged key row (+ pad: conflict-free reads)
-    // bytes per staged V^T row: 8 more than the 128 of a row's keys, so the
-    // 16 rows that one pass of an 8-byte read touches start on distinct
-    // bank pairs
-    static constexpr int kRowV = kKeys * 2 + 8;
+    // bytes per staged value row ([key][d], natural order): 32 more than the
+    // row's 2D, so the four consecutive keys one transpose read touches
+    // start 32 bytes apart modulo 128 (distinct banks)
+    static constexpr int kRowV = D * 2 + 32;
     static constexpr int kBytesK = kKeys * kRowK;
-    static constexpr int kBytesV = 2 * D * kRowV;
+    static constexpr int kBytesV = 2 * kKeys * kRowV;
 };
 
 // The 64 queries of query block qb against every key they see.  All threads
@@ -109,14 +121,14 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
         const int64_t last_q = qb * kQBlock + kQBlock - 1;
         if (last_q + diag + 1 < kend) kend = last_q + diag + 1;
     }
-    // Per chunk a thread moves KP 16-byte pieces of keys and VP (4 keys x 8 d)
-    // blocks of values; the next chunk's pieces are loaded into registers
+    // Per chunk a thread moves KP 16-byte pieces of keys and VP of values
+    // (8 d of one key); the next chunk's pieces are loaded into registers
     // while the current chunk is multiplied.
     constexpr int KP = kKeys * (D2 / 8) / kThreads;
-    constexpr int VN = 2 * (kKeys / 4) * (D / 8);        // value blocks per chunk
-    constexpr int VP = (VN + kThreads - 1) / kThreads;
-    static_assert(KP * kThreads == kKeys * (D2 / 8), "staging split");
-    uint4 kreg[KP], vreg[VP][4];
+    constexpr int VN = 2 * kKeys * (D / 8);  // value pieces per chunk
+    constexpr int VP = VN / kThreads;
+    static_assert(KP * kThreads == kKeys * (D2 / 8) && VP * kThreads == VN, "staging split");
+    uint4 kreg[KP], vreg[VP];
     // guard = false: the chunk lies inside the keys (every chunk but a
     // ragged last one), so its loads need no bounds checks
     auto load_chunk_g = [&](int64_t c0, bool guard) {
@@ -132,15 +144,12 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
 #pragma unroll
         for (int i = 0; i < VP; ++i) {
             const int p = i * kThreads + threadIdx.x;
-            const int comp = p / ((kKeys / 4) * (D / 8));
-            const int rem = p - comp * (kKeys / 4) * (D / 8);
-            const int key0 = 4 * (rem % (kKeys / 4)), d0 = 8 * (rem / (kKeys / 4));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t kj = c0 + key0 + r;
-                const uint4* src = reinterpret_cast<const uint4*>((comp ? a.v_im : a.v_re) + (h * a.sk + kj) * D + d0);
-                vreg[i][r] = (p < VN && (!guard || kj < a.sk)) ? *src : make_uint4(0, 0, 0, 0);
-            }
+            const int comp = p / (kKeys * (D / 8));
+            const int rem = p - comp * kKeys * (D / 8);
+            const int key = rem / (D / 8), d0 = 8 * (rem % (D / 8));
+            const int64_t kj = c0 + key;
+            const uint4* src = reinterpret_cast<const uint4*>((comp ? a.v_im : a.v_re) + (h * a.sk + kj) * D + d0);
+            vreg[i] = (!guard || kj < a.sk) ? *src : make_uint4(0, 0, 0, 0);
         }
     };
     auto load_chunk = [&](int64_t c0) {
@@ -156,26 +165,13 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
             const int key = p / (D2 / 8), dim0 = 8 * (p % (D2 / 8));
             *reinterpret_cast<uint4*>(s_k + key * kRowK + dim0 * 2) = kreg[i];
         }
-        // values transposed: 4 keys x 8 d -> 8 rows of 4 consecutive keys
 #pragma unroll
         for (int i = 0; i < VP; ++i) {
             const int p = i * kThreads + threadIdx.x;
-            if (p >= VN) continue;
-            const int comp = p / ((kKeys / 4) * (D / 8));
-            const int rem = p - comp * (kKeys / 4) * (D / 8);
-            // 16 consecutive threads write one V^T row's 128 bytes
-            const int key0 = 4 * (rem % (kKeys / 4)), d0 = 8 * (rem / (kKeys / 4));
-            const uint32_t w[4][4] = {{vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w},
-                                      {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w},
-                                      {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w},
-                                      {vreg[i][3].x, vreg[i][3].y, vreg[i][3].z, vreg[i][3].w}};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sh = 16 * (e & 1);
-                const uint32_t k01 = ((w[0][e >> 1] >> sh) & 0xFFFFu) | (((w[1][e >> 1] >> sh) & 0xFFFFu) << 16);
-                const uint32_t k23 = ((w[2][e >> 1] >> sh) & 0xFFFFu) | (((w[3][e >> 1] >> sh) & 0xFFFFu) << 16);
-                *reinterpret_cast<uint2*>(s_v + (comp * D + d0 + e) * kRowV + key0 * 2) = make_uint2(k01, k23);
-            }
+            const int comp = p / (kKeys * (D / 8));
+            const int rem = p - comp * kKeys * (D / 8);
+            const int key = rem / (D / 8), d0 = 8 * (rem % (D / 8));
+            *reinterpret_cast<uint4*>(s_v + (comp * kKeys + key) * kRowV + d0 * 2) = vreg[i];
         }
     };
     if (kend > 0) load_chunk(0);
@@ -263,14 +259,20 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t qb, uint8_t* 
             }
             const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
             const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-            const int key_a = 32 * ks + 4 * g, key_b = key_a + 16;
+            // A operand of O^T: lane l needs V[key][16t + l % 16] for keys
+            // 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3.  A transpose read
+            // gives lane i of a 16-lane group element i % 4 of the 8 bytes
+            // lane 4k + i/4 addresses, as its element k; so lane j of the
+            // group addresses key kb + j/4, d 16t + 4(j % 4).
+            const int key_a = 32 * ks + 4 * g + (c16 >> 2), key_b = key_a + 16;
+            const int dq = 4 * (c16 & 3);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int t = 0; t < DT; ++t) {
-                    const uint8_t* row = s_v + (c * D + 16 * t + c16) * kRowV;
-                    const uint2 va = *reinterpret_cast<const uint2*>(row + key_a * 2);
-                    const uint2 vb = *reinterpret_cast<const uint2*>(row + key_b * 2);
+                    const uint8_t* base = s_v + (size_t)(c * kKeys) * kRowV + (16 * t + dq) * 2;
+                    const uint2 va = ds_read_tr16(base + key_a * kRowV);
+                    const uint2 vb = ds_read_tr16(base + key_b * kRowV);
                     const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(va.x, va.y, vb.x, vb.y));
                     o[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, ph, o[c][t], 0, 0, 0);
                     o[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl, o[c][t], 0, 0, 0);
