@@ -77,6 +77,7 @@ CASES = [
     (3, False, 17, 1360, 2),     # P = 3, ragged last group
     (3, True, 40, 2048, 16),     # P = 6, the 2048-column shape
     (3, True, 9, 1024, 64),      # P = 6, batch 64
+    (2, True, 9, 1024, 64),      # P = 4, batch 64 in chunks of 4 (int8: the one-row-per-wave kernel)
 ]
 
 
@@ -193,6 +194,22 @@ def test_llama_attention_shape_s2(B):
     log(f"widely-linear 4096x4096 -> 2048x2048 S=2 B={B}")
     layer, codes, scales = widely_linear_case(4096, 4096, 200, 2)
     check_float(layer, codes, scales, 2, True, B, F.FAIRY_BF16, 201)
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_llama_attention_shape_s2_int8(B):
+    """The 2048x2048 decode layer with int8 activations: the raw int32
+    accumulators of 64 sampled rows equal the oracle's exact sums, and every
+    output is within the float bound."""
+    log(f"widely-linear 4096x4096 -> 2048x2048 S=2 int8 B={B}")
+    layer, codes, scales = widely_linear_case(4096, 4096, 200, 2)
+    xr, xi = synth.int8_uniform((B, 2048), 205 + B)
+    yr, yi, acc = run_gemv(layer, dev(xr), dev(xi), F.FAIRY_I8, B, want_acc=True)
+    rows = np.sort(synth.rng(206).choice(2048, 64, replace=False))
+    want_acc = oracle.cgemv_acc_i64(codes[:, rows], xr, xi)
+    assert np.array_equal(acc[:, :, :, rows].astype(np.int64), want_acc)
+    wr, wi = oracle.cgemv_dense(codes, scales, 2, True, xr.astype(np.float64), xi.astype(np.float64))
+    assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
 
 
 @pytest.mark.parametrize("rows,cols,seed", [(11008, 4096, 300), (4096, 11008, 302)])
