@@ -66,6 +66,20 @@ def test_cattention_sharp_scores():
     assert rel_l2(o_re + 1j * o_im, w_re + 1j * w_im) <= TOL
 
 
+@pytest.mark.parametrize("scale,causal", [(-0.3, 0), (-1.0, 1), (0.0, 1)])
+def test_cattention_negative_and_zero_scale(scale, causal):
+    """A negative scale favours the lowest scores (applied as a positive one
+    to the negated queries); a zero scale weights every visible key equally."""
+    h, sq, sk, d = 2, 70, 130, 64
+    log(f"cattention scale={scale} causal={causal}")
+    bits, v = make(h, sq, sk, d, 55)
+    o_re, o_im = run(bits, h, sq, sk, d, scale, causal)
+    w_re, w_im = oracle.cattention(*v, scale, bool(causal))
+    err = rel_l2(o_re + 1j * o_im, w_re + 1j * w_im)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
+
+
 def test_cattention_llama_prefill_sampled_heads():
     """LLaMA-2-7B attention at prefill: 32 heads, 2048 tokens, real head dim
     128 (complex d = 64), causal; the oracle checks heads 0 and 31."""
