@@ -303,6 +303,13 @@ def main():
     if not (torch.equal(y_re, eager_y[0]) and torch.equal(y_im, eager_y[1])):
         raise SystemExit("graph replay output differs from the eager GEMV output")
     gbs = packed_bytes / (ms * 1e-3) / 1e9
+    # this box's streaming ceiling: a 256 MiB device copy (bytes read + written)
+    csrc = torch.empty((64 << 20,), dtype=torch.int32, device="cuda")
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    copy_ms = bn.ev_time(lambda i: cdst.copy_(csrc), 10)
+    copy_gbs = 2 * csrc.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del csrc, cdst
     alg_bytes = packed_bytes + B * m * 2 * 2 + B * n * 2 * 4
     hbm_achieved = alg_bytes / (ms * 1e-3) / 1e9
     # the multiplication-free form: two fp32 adds per code per batch column
@@ -346,7 +353,9 @@ def main():
             "kernel": GEMV_KERNEL,
             "alg_adds_per_launch": alg_adds,
             "hbm": {"achieved": round(hbm_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(hbm_achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes},
+                    "frac": round(hbm_achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes,
+                    "measured_copy_GBps": round(copy_gbs, 1),
+                    "frac_of_measured_copy": round(hbm_achieved / copy_gbs, 4)},
             "eager_ms_per_call": eager_ms,
         },
     }
