@@ -7,8 +7,9 @@
 // gives real weights, and the values' real and imaginary parts are averaged
 // with them separately.
 //
-// One pass, online softmax (FlashAttention style).  A block is 4 waves over
-// 64 queries of one head; each wave owns 16 queries and walks the keys in
+// One pass, online softmax (FlashAttention style).  A block is 8 waves over
+// 128 queries of one head (each staged key chunk serves 128 queries); each
+// wave owns 16 queries and walks the keys in
 // chunks of 64 staged in LDS (keys as [key][re | im], values as
 // [re/im][key][d], both copied as they are in memory).
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
@@ -33,7 +34,7 @@ namespace attn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQBlock = 16 * kWaves;  // queries per block
 constexpr int kKeys = 64;             // keys per chunk
