@@ -41,6 +41,9 @@ CASES = [
     (1, 130, 130, 64, 1),        # three query blocks, three key chunks
     (4, 5, 1, 32, 0),            # a single key: o = v
     (1, 200, 260, 128, 0),
+    (2, 257, 1000, 64, 1),       # causal, two query blocks per head, ragged tail chunk
+    (1, 129, 640, 32, 0),        # keys a whole number of chunks, ragged queries
+    (1, 300, 333, 128, 1),
 ]
 
 
@@ -56,14 +59,19 @@ def test_cattention(h, sq, sk, d, causal):
     assert err <= TOL
 
 
-def test_cattention_sharp_scores():
-    """Scores spread over tens of units: the online softmax's rescaling and
-    the exp of large negative arguments are exercised."""
-    h, sq, sk, d = 2, 64, 192, 64
+@pytest.mark.parametrize("scale,causal,sk", [(1.0, 0, 192), (3.0, 1, 700)])
+def test_cattention_sharp_scores(scale, causal, sk):
+    """Scores spread over tens of units: the running maximum moves by more
+    than the lazy threshold mid-sequence, so the output rescaling and the
+    exp of large negative arguments are exercised."""
+    h, sq, d = 2, 64 if not causal else 300, 64
+    log(f"cattention sharp scale={scale} causal={causal} sk={sk}")
     bits, v = make(h, sq, sk, d, 77)
-    o_re, o_im = run(bits, h, sq, sk, d, 1.0, 0)
-    w_re, w_im = oracle.cattention(*v, 1.0, False)
-    assert rel_l2(o_re + 1j * o_im, w_re + 1j * w_im) <= TOL
+    o_re, o_im = run(bits, h, sq, sk, d, scale, causal)
+    w_re, w_im = oracle.cattention(*v, scale, bool(causal))
+    err = rel_l2(o_re + 1j * o_im, w_re + 1j * w_im)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
 
 
 @pytest.mark.parametrize("scale,causal", [(-0.3, 0), (-1.0, 1), (0.0, 1)])
