@@ -14,15 +14,22 @@ namespace {
 // plane's exact totals (the raw accumulators), and a second one over the
 // distances below P adds the scaled planes in float.
 // ---------------------------------------------------------------------------
+// Distances 4 and 8 inside a 16-lane row are DPP row rotations (lane i
+// adds lane i - 4, then i - 8, modulo the row): each lane then holds the sum
+// of its residue class, added in a lane-dependent order, which is exact for
+// integers.
+__device__ __forceinline__ int dpp_ror4(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false); }
+
 template <int P>
 __device__ __forceinline__ int plane_total(int v)
 {
     if (P <= 1) v += dpp_xor1(v);
     if (P <= 2) v += dpp_xor2(v);
-    if (P <= 4) v += swz_xor4(v);
-    if (P <= 8) v += swz_xor8(v);
-    if (P <= 16) v += swz_xor16(v);
-    if (P <= 32) v += __shfl_xor(v, 32);
+    if (P <= 4) v += dpp_ror4(v);
+    if (P <= 8) v += dpp_ror8(v);
+    if (P <= 16) v = swap16_add(v);
+    if (P <= 32) v = swap32_add(v);
     return v;
 }
 

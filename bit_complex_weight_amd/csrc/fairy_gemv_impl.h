@@ -19,7 +19,7 @@
 // lane decodes 64 codes with bit operations (decode_bf16_pair), multiplies
 // nothing, accumulates A1..A4 with v_dot2_f32_bf16 (bf16) or fp32 FMAs on the
 // +-2 / 0 decoded values (fp32), and folds the plane's scales in once.  Row
-// partial sums are combined across the TROW lanes with DPP / ds_swizzle
+// partial sums are combined across the TROW lanes with DPP / row-swap
 // butterflies: deterministic, no atomics.
 //
 // When the plane count P divides 64 and a row has at least 64 units, a wave

@@ -1,7 +1,7 @@
 // fairy_internal.h -- shared declarations of the HIP library (not installed).
 //
 // Device helpers common to the kernels: the 2-bit code decode and the
-// cross-lane (DPP / ds_swizzle) reductions.  Host launchers are declared at
+// cross-lane (DPP / row-swap) reductions.  Host launchers are declared at
 // the bottom; fairy_api.hip validates arguments and calls them.
 #pragma once
 
@@ -51,26 +51,54 @@ __device__ __forceinline__ int i8_group_col(int s, int b)
 
 // ---------------------------------------------------------------------------
 // Cross-lane sums over aligned groups of W lanes (W = 2..64), result in every
-// lane of the group.  Butterflies: DPP quad_perm for distances 1 and 2,
-// ds_swizzle (bit mode, xor) for 4, 8, 16 and a bpermute for 32.  Every lane
-// adds the same pair of operands at every step, so all lanes of a group hold
+// lane of the group, all in VALU instructions (no LDS round trips):
+//   distance 1, 2: DPP quad_perm (xor 1, xor 2);
+//   8-lane halves: DPP row_half_mirror (lane i <-> 7 - i: after the quad
+//     steps every lane of a quad holds the quad's sum, so this adds the
+//     other quad of the half);
+//   16-lane rows: DPP row_mirror (lane i <-> 15 - i, the other half);
+//   32 and 64: v_permlane16_swap / v_permlane32_swap (rows 0 <-> 1 and
+//     2 <-> 3; the two halves of the wave).
+// At every step the two lanes of a pair add the same two values (in either
+// order: addition is commutative), so all lanes of a group hold
 // bit-identical results.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int dpp_xor1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_xor2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ int swz_xor4(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x101F); }
-__device__ __forceinline__ int swz_xor8(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x201F); }
-__device__ __forceinline__ int swz_xor16(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
+__device__ __forceinline__ int dpp_half_mirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_mirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); }
+
+// x + (the value of the lane 16 or 32 away), identical in both lanes
+__device__ __forceinline__ float swap16_add(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_add(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ int swap16_add(int v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)(r[0] + r[1]);
+}
+__device__ __forceinline__ int swap32_add(int v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)(r[0] + r[1]);
+}
 
 template <int W>
 __device__ __forceinline__ float group_sum(float v)
 {
     v += __int_as_float(dpp_xor1(__float_as_int(v)));
     if (W >= 4) v += __int_as_float(dpp_xor2(__float_as_int(v)));
-    if (W >= 8) v += __int_as_float(swz_xor4(__float_as_int(v)));
-    if (W >= 16) v += __int_as_float(swz_xor8(__float_as_int(v)));
-    if (W >= 32) v += __int_as_float(swz_xor16(__float_as_int(v)));
-    if (W >= 64) v += __shfl_xor(v, 32);
+    if (W >= 8) v += __int_as_float(dpp_half_mirror(__float_as_int(v)));
+    if (W >= 16) v += __int_as_float(dpp_mirror(__float_as_int(v)));
+    if (W >= 32) v = swap16_add(v);
+    if (W >= 64) v = swap32_add(v);
     return v;
 }
 
@@ -79,10 +107,10 @@ __device__ __forceinline__ int group_sum_i(int v)
 {
     v += dpp_xor1(v);
     if (W >= 4) v += dpp_xor2(v);
-    if (W >= 8) v += swz_xor4(v);
-    if (W >= 16) v += swz_xor8(v);
-    if (W >= 32) v += swz_xor16(v);
-    if (W >= 64) v += __shfl_xor(v, 32);
+    if (W >= 8) v += dpp_half_mirror(v);
+    if (W >= 16) v += dpp_mirror(v);
+    if (W >= 32) v = swap16_add(v);
+    if (W >= 64) v = swap32_add(v);
     return v;
 }
 
