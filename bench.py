@@ -166,7 +166,7 @@ class Bench:
         f(0)
         return attention_entry(self.ev_time(f, iters), h, sq, sk, d, causal)
 
-    def gemm_rate(self, L, desc, M, xdtype, algo, iters=5, seed=204):
+    def gemm_rate(self, L, desc, M, xdtype, algo, iters=5, seed=204, graph=False):
         torch, F = self.torch, self.F
         n, m = L["n"], L["m"]
         if xdtype == F.FAIRY_I8:
@@ -178,6 +178,8 @@ class Bench:
         yi = torch.empty((M, n), dtype=torch.float32, device="cuda")
         f = lambda i: F.fairy_cgemm(desc, xr, xi, xdtype, M, m, yr, yi, n, None, algo)
         f(0)
+        if graph:  # short kernels: time graph replays, not host launches
+            return self.graph_time(f, iters)[0]
         return self.ev_time(f, iters)
 
 
@@ -188,12 +190,12 @@ def attention_entry(ms, h, sq, sk, d, causal):
     processed 64-key chunk (the weights go through two bf16 MFMAs)."""
     if causal:
         pairs = sum(min(sk, i + (sk - sq) + 1) for i in range(sq))
-        # a block of 64 queries walks the 64-key chunks up to its last query's diagonal
-        mfma_pairs = sum(((min(sk, qb * 64 + 64 + (sk - sq)) + 63) // 64) * 64 * 64
-                         for qb in range((sq + 63) // 64))
+        # a block of 128 queries walks the 64-key chunks up to its last query's diagonal
+        mfma_pairs = sum(((min(sk, qb * 128 + 128 + (sk - sq)) + 63) // 64) * 64 * 128
+                         for qb in range((sq + 127) // 128))
     else:
         pairs = sq * sk
-        mfma_pairs = ((sq + 63) // 64) * 64 * ((sk + 63) // 64) * 64
+        mfma_pairs = ((sq + 127) // 128) * 128 * ((sk + 63) // 64) * 64
     alg = 8.0 * h * pairs * d
     mf = 12.0 * h * mfma_pairs * d
     t = ms * 1e-3
@@ -416,6 +418,10 @@ def main():
             del L2
             torch.cuda.empty_cache()
         d0 = F.make_clinear(n, m, S, 1, L["packed"], L["scales"])
+        # the matrix-core GEMM at decode batch sizes, beside the VALU GEMV rows
+        for mm in (16, 64):
+            msg = bn.gemm_rate(L, d0, mm, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA, iters=100, graph=True)
+            rows_out[f"gemm_2048x2048_M{mm}_bf16_mfma"] = gemm_entry(msg, P, n, m, mm, MFMA_PEAK_TFLOPS["bf16"])
         for dt, dn in ((F.FAIRY_BF16, "bf16"), (F.FAIRY_I8, "i8")):
             msg = bn.gemm_rate(L, d0, 2048, dt, F.FAIRY_ALGO_MFMA)
             rows_out[f"gemm_2048x2048_M2048_{dn}_mfma"] = gemm_entry(msg, P, n, m, 2048, MFMA_PEAK_TFLOPS[dn])
