@@ -311,7 +311,15 @@ def main():
     cdst.copy_(csrc)
     copy_ms = bn.ev_time(lambda i: cdst.copy_(csrc), 10)
     copy_gbs = 2 * csrc.numel() * 4 / (copy_ms * 1e-3) / 1e9
-    del csrc, cdst
+    # and its streaming-read rate: row sums of 512 MiB as [32768][4096] fp32
+    # (512 MiB read, 128 KiB written; the fastest of the torch reductions
+    # tried here)
+    rsrc = torch.ones((32768, 4096), dtype=torch.float32, device="cuda")
+    rsum = torch.empty((32768,), dtype=torch.float32, device="cuda")
+    torch.sum(rsrc, dim=1, out=rsum)
+    read_ms = bn.ev_time(lambda i: torch.sum(rsrc, dim=1, out=rsum), 10)
+    read_gbs = rsrc.numel() * 4 / (read_ms * 1e-3) / 1e9
+    del csrc, cdst, rsrc, rsum
     alg_bytes = packed_bytes + B * m * 2 * 2 + B * n * 2 * 4
     hbm_achieved = alg_bytes / (ms * 1e-3) / 1e9
     # the multiplication-free form: two fp32 adds per code per batch column
@@ -357,7 +365,9 @@ def main():
             "hbm": {"achieved": round(hbm_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(hbm_achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes,
                     "measured_copy_GBps": round(copy_gbs, 1),
-                    "frac_of_measured_copy": round(hbm_achieved / copy_gbs, 4)},
+                    "frac_of_measured_copy": round(hbm_achieved / copy_gbs, 4),
+                    "measured_read_GBps": round(read_gbs, 1),
+                    "frac_of_measured_read": round(hbm_achieved / read_gbs, 4)},
             "eager_ms_per_call": eager_ms,
         },
     }
