@@ -471,10 +471,10 @@ __global__ __launch_bounds__(kThreads) void k_cattention(Args a)
     // them so each XCD takes a contiguous run of (head, query block) pairs:
     // the few heads an XCD works on at a time keep their keys and values in
     // its own L2.
-    const uint32_t nx = gridDim.x, total = nx * gridDim.y;
-    uint32_t id = blockIdx.y * nx + blockIdx.x;
+    const uint64_t nx = gridDim.x, total = nx * gridDim.y;
+    uint64_t id = blockIdx.y * nx + blockIdx.x;
     if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
-    const int64_t h = id / nx, x = id % nx;
+    const int64_t h = (int64_t)(id / nx), x = (int64_t)(id % nx);
     if (!a.causal) {
         attend_tile<D>(a, h, x, s_k, s_v);
         return;
