@@ -24,8 +24,8 @@
  *   [iFairy press article] bestcxt.com, §三: attention scores are the real
  *       part of the Hermitian inner product (a real number for the softmax).
  *
- * Readings taken where the pages are silent are listed in the design doc and
- * repeated next to the function they affect.
+ * Readings taken where the pages are silent are stated next to the
+ * function they affect.
  *
  * Parity pins (the tests that tie this oracle to something other than
  * itself) live in tests/test_oracle_*.py.
