@@ -166,7 +166,7 @@ class Bench:
         f(0)
         return attention_entry(self.ev_time(f, iters), h, sq, sk, d, causal)
 
-    def gemm_rate(self, L, desc, M, xdtype, algo, iters=5, seed=204, graph=False):
+    def gemm_rate(self, L, desc, M, xdtype, algo, iters=5, seed=204, graph=False, workspace=False):
         torch, F = self.torch, self.F
         n, m = L["n"], L["m"]
         if xdtype == F.FAIRY_I8:
@@ -176,7 +176,11 @@ class Bench:
         xr, xi = self.dev(xr), self.dev(xi)
         yr = torch.empty((M, n), dtype=torch.float32, device="cuda")
         yi = torch.empty((M, n), dtype=torch.float32, device="cuda")
-        f = lambda i: F.fairy_cgemm(desc, xr, xi, xdtype, M, m, yr, yi, n, None, algo)
+        ws, wsb = None, 0
+        if workspace:  # the optional K-split partial sums
+            wsb = F.fairy_cgemm_workspace_bytes(desc, M, xdtype, algo)
+            ws = torch.empty((max(wsb, 16),), dtype=torch.uint8, device="cuda")
+        f = lambda i: F.fairy_cgemm(desc, xr, xi, xdtype, M, m, yr, yi, n, None, algo, ws, wsb)
         f(0)
         if graph:  # short kernels: time graph replays, not host launches
             return self.graph_time(f, iters)[0]
@@ -428,10 +432,15 @@ def main():
             del L2
             torch.cuda.empty_cache()
         d0 = F.make_clinear(n, m, S, 1, L["packed"], L["scales"])
-        # the matrix-core GEMM at decode batch sizes, beside the VALU GEMV rows
+        # the matrix-core GEMM at decode batch sizes, beside the VALU GEMV
+        # rows: one launch over 32 row blocks, and split along K (with the
+        # optional workspace) to fill the chip
         for mm in (16, 64):
             msg = bn.gemm_rate(L, d0, mm, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA, iters=100, graph=True)
             rows_out[f"gemm_2048x2048_M{mm}_bf16_mfma"] = gemm_entry(msg, P, n, m, mm, MFMA_PEAK_TFLOPS["bf16"])
+            msg = bn.gemm_rate(L, d0, mm, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA, iters=100, graph=True, workspace=True)
+            rows_out[f"gemm_2048x2048_M{mm}_bf16_mfma_splitk"] = gemm_entry(msg, P, n, m, mm,
+                                                                           MFMA_PEAK_TFLOPS["bf16"])
         for dt, dn in ((F.FAIRY_BF16, "bf16"), (F.FAIRY_I8, "i8")):
             msg = bn.gemm_rate(L, d0, 2048, dt, F.FAIRY_ALGO_MFMA)
             rows_out[f"gemm_2048x2048_M2048_{dn}_mfma"] = gemm_entry(msg, P, n, m, 2048, MFMA_PEAK_TFLOPS[dn])

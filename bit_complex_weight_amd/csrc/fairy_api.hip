@@ -244,11 +244,12 @@ fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x
     fairy_status st = check_layer_call(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, &la);
     if (st != FAIRY_OK) return st;
     if (algo == FAIRY_ALGO_MFMA && xdtype == FAIRY_F32) return FAIRY_ERR_UNSUPPORTED;
+    // the workspace is optional: without one the call runs unsplit
     const size_t need = fairy::cgemm_workspace_bytes(la, M, xdtype, algo);
-    if (need && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return FAIRY_ERR_WORKSPACE;
+    if (workspace && need && (workspace_bytes < need || !aligned(workspace, 16))) return FAIRY_ERR_WORKSPACE;
     clear_stale_error();
-    hipError_t e = fairy::launch_cgemm(la, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, algo, workspace,
-                                       as_stream(stream));
+    hipError_t e = fairy::launch_cgemm(la, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, algo,
+                                       need ? workspace : nullptr, as_stream(stream));
     if (e == hipErrorNotSupported) return FAIRY_ERR_UNSUPPORTED;
     return from_hip(e);
 }
@@ -290,7 +291,6 @@ fairy_status fairy_cgemm_rope(const fairy_clinear* L, const void* x_re, const vo
     if (st != FAIRY_OK) return st;
     if (algo == FAIRY_ALGO_MFMA && xdtype == FAIRY_F32) return FAIRY_ERR_UNSUPPORTED;
     if ((st = check_rope(positions, head_dim, base, &la)) != FAIRY_OK) return st;
-    if (fairy::cgemm_workspace_bytes(la, M, xdtype, algo)) return FAIRY_ERR_UNSUPPORTED;
     clear_stale_error();
     hipError_t e = fairy::launch_cgemm(la, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, nullptr, algo, nullptr,
                                        as_stream(stream));

@@ -6,26 +6,28 @@
 
 namespace fairy {
 
+static bool uses_mfma(int64_t M, int32_t xdtype, int32_t algo)
+{
+    const bool mfma_ok = xdtype == FAIRY_BF16 || xdtype == FAIRY_I8;
+    return (algo == FAIRY_ALGO_MFMA) || (algo == FAIRY_ALGO_AUTO && mfma_ok && M >= 32);
+}
+
+// The matrix-core path at token counts that leave CUs idle splits K and
+// keeps the partial sums here; every other path needs none.
 size_t cgemm_workspace_bytes(const LayerArgs& L, int64_t M, int32_t xdtype, int32_t algo)
 {
-    (void)L;
-    (void)M;
-    (void)xdtype;
-    (void)algo;
-    return 0;
+    if (!uses_mfma(M, xdtype, algo) || (xdtype != FAIRY_BF16 && xdtype != FAIRY_I8)) return 0;
+    return cgemm_mfma_workspace_bytes(L.n, L.m, M, L.planes, xdtype);
 }
 
 hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype, int64_t M,
                         int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,
                         void* workspace, hipStream_t s)
 {
-    (void)workspace;
-    const bool mfma_ok = xdtype == FAIRY_BF16 || xdtype == FAIRY_I8;
-    const bool use_mfma = (algo == FAIRY_ALGO_MFMA) || (algo == FAIRY_ALGO_AUTO && mfma_ok && M >= 32);
-    if (use_mfma) {
-        if (!mfma_ok) return hipErrorNotSupported;
+    if (uses_mfma(M, xdtype, algo)) {
+        if (xdtype != FAIRY_BF16 && xdtype != FAIRY_I8) return hipErrorNotSupported;
         const gemv::GemvArgs a = gemv::make_args(L, x_re, x_im, M, ldx, y_re, y_im, ldy, acc);
-        return launch_cgemm_mfma(a, xdtype, s);
+        return launch_cgemm_mfma(a, xdtype, workspace, s);
     }
     // VALU path: the decode kernel streams the token rows through LDS in
     // chunks, re-reading the (L2-resident) codes per chunk.

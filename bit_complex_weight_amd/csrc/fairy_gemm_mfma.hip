@@ -172,7 +172,7 @@ struct CodeRows {
 template <int Q, typename Acc>
 __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, const Acc (&acc)[4][kTT][kRT], int p,
                                             int slot, int rg, int row0, int tok0, int q, int r16, int lane,
-                                            int accumulate)
+                                            int accumulate, float* part)
 {
     // This plane's contribution.  U planes: y_re += s_re A1 - s_im A2,
     // y_im += s_re A3 + s_im A4; W planes multiply conj(x): A2 and A3 flip.
@@ -241,6 +241,26 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
         }
     }
     if (slot != 0) return;
+    if (part) {
+        // split K: this block's share of the sum, [split][re/im][M][n]
+        const int64_t mn = (int64_t)a.B * a.n;
+        float* pre = part + (int64_t)blockIdx.z * 2 * mn;
+#pragma unroll
+        for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+            for (int rt = 0; rt < kRT; ++rt) {
+                const int row = row0 + 16 * rt + r16;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int tok = tok0 + 16 * tt + 4 * q + v;
+                    if (row < a.n && tok < a.B) {
+                        pre[(int64_t)tok * a.n + row] = pr[tt][rt][v];
+                        pre[mn + (int64_t)tok * a.n + row] = pi[tt][rt][v];
+                    }
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt)
 #pragma unroll
@@ -263,7 +283,8 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
 }
 
 template <int XT, int Q>
-__global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_base, int plane0, int accumulate)
+__global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_base, int plane0, int accumulate,
+                                                         int chunks_per_split, float* part)
 {
     using G_ = Geo<XT>;
     using Frag = typename G_::Frag;
@@ -287,20 +308,24 @@ __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_bas
 #pragma unroll
             for (int j = 0; j < kRT; ++j) acc[b][i][j] = Acc{0, 0, 0, 0};
 
+    // this block's chunks of the K range: all of them, or one split's share
     const int nchunk = (G + NG - 1) / NG;
-    dma_chunk<XT>(a, tok0, 0, lds, wave, lane);
+    const int ch0 = blockIdx.z * chunks_per_split;
+    const int ch1 = (nchunk < ch0 + chunks_per_split) ? nchunk : ch0 + chunks_per_split;
+    dma_chunk<XT>(a, tok0, ch0 * G_::cols, lds, wave, lane);
     uint32_t cw[kRT][NG];
-    codes.chunk(0, cw);
+    codes.chunk(ch0 * NG, cw);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int ch = 0; ch < nchunk; ++ch) {
+    for (int ch = ch0; ch < ch1; ++ch) {
+        const int buf = (ch - ch0) & 1;
         // the next chunk streams into the other buffer, which every wave
         // finished reading before the barrier that ended the previous chunk
-        if (ch + 1 < nchunk) dma_chunk<XT>(a, tok0, (ch + 1) * G_::cols, lds + ((ch + 1) & 1) * kBufBytes, wave, lane);
+        if (ch + 1 < ch1) dma_chunk<XT>(a, tok0, (ch + 1) * G_::cols, lds + (buf ^ 1) * kBufBytes, wave, lane);
         uint32_t nw[kRT][NG];
         codes.chunk((ch + 1) * NG, nw);
-        const uint8_t* xb = lds + (ch & 1) * kBufBytes;
+        const uint8_t* xb = lds + buf * kBufBytes;
         // A group past the end has zero activations and zero code words, so
         // its products are exactly zero: the chunk needs no branch.
         Frag xf[2][2][kTT];
@@ -347,25 +372,91 @@ __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_bas
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into the other buffer have landed
         __syncthreads();
     }
-    finish_tile<Q>(a, reinterpret_cast<floatx4_t*>(lds), acc, p, slot, rg, row0, tok0, q, r16, lane, accumulate);
+    finish_tile<Q>(a, reinterpret_cast<floatx4_t*>(lds), acc, p, slot, rg, row0, tok0, q, r16, lane, accumulate,
+                   part);
+}
+
+// Split K: y = (accumulate ? y : 0) + the splits' partial sums, added in
+// split order (deterministic), then the optional rotation.
+__global__ __launch_bounds__(256) void k_split_sum(GemvArgs a, const float* part, int splits, int accumulate)
+{
+    const int64_t mn = (int64_t)a.B * a.n;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= mn) return;
+    const int tok = (int)(idx / a.n), row = (int)(idx % a.n);
+    float sr = 0.0f, si = 0.0f;
+    for (int z = 0; z < splits; ++z) {
+        sr += part[2 * z * mn + idx];
+        si += part[(2 * z + 1) * mn + idx];
+    }
+    float* yr = a.y_re + (int64_t)tok * a.ldy + row;
+    float* yi = a.y_im + (int64_t)tok * a.ldy + row;
+    float fr = accumulate ? *yr + sr : sr;
+    float fi = accumulate ? *yi + si : si;
+    gemv::rope_apply(a, row, tok, fr, fi);
+    *yr = fr;
+    *yi = fi;
+}
+
+// Groups per staged chunk and chunks of a row, by activation type
+template <int XT>
+constexpr int chunk_groups() { return Geo<XT>::groups; }
+
+int split_count(int64_t n, int64_t m, int64_t M, int P, int xdtype)
+{
+    // A single pass (P planes in one launch) that leaves CUs idle is split
+    // along K: each split walks a share of the chunks and the shares are
+    // added by a second kernel.
+    if (P != 1 && P != 2 && P != 4) return 1;
+    const int Q = P;
+    const int64_t rows = (kWaves / Q) * kWaveRows;
+    const int64_t blocks = ((n + rows - 1) / rows) * ((M + kTok - 1) / kTok);
+    const int64_t G = m / 64;
+    const int ng = xdtype == FAIRY_BF16 ? chunk_groups<FAIRY_BF16>() : chunk_groups<FAIRY_I8>();
+    const int64_t nchunk = (G + ng - 1) / ng;
+    constexpr int64_t kTargetBlocks = 256;  // one block per CU (two waves per SIMD)
+    if (blocks >= kTargetBlocks / 2 || nchunk < 2) return 1;
+    int64_t splits = (kTargetBlocks + blocks - 1) / blocks;
+    if (splits > nchunk) splits = nchunk;
+    const int64_t cps = (nchunk + splits - 1) / splits;
+    return (int)((nchunk + cps - 1) / cps);
 }
 
 template <int XT, int Q>
-hipError_t launch_pass(const GemvArgs& a, int plane0, int accumulate, hipStream_t s)
+hipError_t launch_pass(const GemvArgs& a, int plane0, int accumulate, float* part, int splits, hipStream_t s)
 {
     const int64_t row_blocks = (a.n + block_rows<Q>() - 1) / block_rows<Q>();
     const int64_t tok_blocks = ((int64_t)a.B + kTok - 1) / kTok;
+    const int nchunk = (a.G + Geo<XT>::groups - 1) / Geo<XT>::groups;
+    if (part) {
+        const int cps = (nchunk + splits - 1) / splits;
+        hipLaunchKernelGGL((k_cgemm_mfma<XT, Q>), dim3((unsigned)row_blocks, (unsigned)tok_blocks, (unsigned)splits),
+                           dim3(kThreads), 0, s, a, 0, plane0, 0, cps, part);
+        const int64_t mn = (int64_t)a.B * a.n;
+        hipLaunchKernelGGL(k_split_sum, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, a, part, splits,
+                           accumulate);
+        return hipGetLastError();
+    }
     for (int64_t tb = 0; tb < tok_blocks; tb += kMaxGridY) {
         const int64_t nb = (tok_blocks - tb < kMaxGridY) ? tok_blocks - tb : kMaxGridY;
         hipLaunchKernelGGL((k_cgemm_mfma<XT, Q>), dim3((unsigned)row_blocks, (unsigned)nb), dim3(kThreads), 0, s, a,
-                           (int)(tb * kTok), plane0, accumulate);
+                           (int)(tb * kTok), plane0, accumulate, nchunk, (float*)nullptr);
     }
     return hipGetLastError();
 }
 
 template <int XT>
-hipError_t launch_all(const GemvArgs& a, hipStream_t s)
+hipError_t launch_all(const GemvArgs& a, void* workspace, hipStream_t s)
 {
+    // split K when a workspace is given, no raw accumulators are asked for,
+    // and the layer is one pass that would leave CUs idle
+    const int splits = split_count(a.n, a.m, a.B, a.P, XT);
+    if (workspace && !a.acc && splits > 1) {
+        float* part = static_cast<float*>(workspace);
+        if (a.P == 4) return launch_pass<XT, 4>(a, 0, 0, part, splits, s);
+        if (a.P == 2) return launch_pass<XT, 2>(a, 0, 0, part, splits, s);
+        return launch_pass<XT, 1>(a, 0, 0, part, splits, s);
+    }
     hipError_t e = hipSuccess;
     for (int p0 = 0; p0 < a.P && e == hipSuccess;) {
         const int rem = a.P - p0;
@@ -373,9 +464,9 @@ hipError_t launch_all(const GemvArgs& a, hipStream_t s)
         const int q = rem >= 4 ? 4 : rem >= 2 ? 2 : 1;
         GemvArgs pass = a;
         if (p0 + q < a.P) pass.pos = nullptr;  // the rotation applies to the finished sum
-        if (q == 4) e = launch_pass<XT, 4>(pass, p0, acc, s);
-        else if (q == 2) e = launch_pass<XT, 2>(pass, p0, acc, s);
-        else e = launch_pass<XT, 1>(pass, p0, acc, s);
+        if (q == 4) e = launch_pass<XT, 4>(pass, p0, acc, nullptr, 1, s);
+        else if (q == 2) e = launch_pass<XT, 2>(pass, p0, acc, nullptr, 1, s);
+        else e = launch_pass<XT, 1>(pass, p0, acc, nullptr, 1, s);
         p0 += q;
     }
     return e;
@@ -383,9 +474,16 @@ hipError_t launch_all(const GemvArgs& a, hipStream_t s)
 
 }  // namespace mfma
 
-hipError_t launch_cgemm_mfma(const gemv::GemvArgs& a, int32_t xdtype, hipStream_t s)
+hipError_t launch_cgemm_mfma(const gemv::GemvArgs& a, int32_t xdtype, void* workspace, hipStream_t s)
 {
-    return (xdtype == FAIRY_BF16) ? mfma::launch_all<FAIRY_BF16>(a, s) : mfma::launch_all<FAIRY_I8>(a, s);
+    return (xdtype == FAIRY_BF16) ? mfma::launch_all<FAIRY_BF16>(a, workspace, s)
+                                  : mfma::launch_all<FAIRY_I8>(a, workspace, s);
+}
+
+size_t cgemm_mfma_workspace_bytes(int64_t n, int64_t m, int64_t M, int32_t P, int32_t xdtype)
+{
+    const int splits = mfma::split_count(n, m, M, P, xdtype);
+    return splits > 1 ? (size_t)splits * 2 * (size_t)M * (size_t)n * sizeof(float) : 0;
 }
 
 }  // namespace fairy

@@ -589,6 +589,9 @@ GemvArgs make_args(const LayerArgs& L, const void* x_re, const void* x_im, int64
 
 }  // namespace gemv
 
-// matrix-core prefill (fairy_gemm_mfma.hip); a.B is the token count
-hipError_t launch_cgemm_mfma(const gemv::GemvArgs& a, int32_t xdtype, hipStream_t s);
+// matrix-core prefill (fairy_gemm_mfma.hip); a.B is the token count.
+// workspace (nullable): fp32 partial sums for the split-K launch, of
+// cgemm_mfma_workspace_bytes() bytes (0: no split for this shape).
+hipError_t launch_cgemm_mfma(const gemv::GemvArgs& a, int32_t xdtype, void* workspace, hipStream_t s);
+size_t cgemm_mfma_workspace_bytes(int64_t n, int64_t m, int64_t M, int32_t P, int32_t xdtype);
 }  // namespace fairy

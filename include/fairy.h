@@ -216,13 +216,21 @@ fairy_status fairy_cgemv_lut(const fairy_clinear* L, const void* x_re, const voi
                              int32_t xdtype, float* y_re, float* y_im,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes fairy_cgemm needs. */
+/* Bytes of the optional fairy_cgemm workspace for these arguments, 0 when
+ * no path uses one.  The matrix-core path at token counts whose 64-row x
+ * 64-token blocks would leave compute units idle (P of 1, 2 or 4 and no acc
+ * requested) splits the K range and keeps fp32 partial sums there:
+ * splits x 2 x M x n floats, added in split order by a second kernel. */
 size_t fairy_cgemm_workspace_bytes(const fairy_clinear* L, int64_t M, int32_t xdtype, int32_t algo);
 
 /* Prefill GEMM: fairy_cgemv over M >= 1 token rows (same semantics, same
  * argument rules with batch replaced by M; acc is [P][4][M][n] for I8).
  * algo: AUTO, VALU (any dtype) or MFMA (BF16 or I8; codes expanded to
- * ternary {-1,0,1} planes feeding the matrix cores). */
+ * ternary {-1,0,1} planes feeding the matrix cores).
+ * workspace: NULL (the call runs without a K split) or at least
+ *   fairy_cgemm_workspace_bytes() bytes, 16-byte aligned, owned by the
+ *   caller and not read before being written (ERR_WORKSPACE if smaller or
+ *   misaligned).  Calls sharing one workspace must not overlap. */
 fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x_im,
                          int32_t xdtype, int64_t M, int64_t ldx,
                          float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,

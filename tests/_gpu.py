@@ -86,7 +86,9 @@ def quantize_widely_linear_on_gpu(u_re, u_im, w_re, w_im, n, m, stages):
     return GpuLayer(n, m, stages, 1, packed, scales), codes, scales
 
 
-def run_gemv(layer, x_re, x_im, xdtype, B, want_acc=False, gemm=False, algo=F.FAIRY_ALGO_AUTO):
+def run_gemv(layer, x_re, x_im, xdtype, B, want_acc=False, gemm=False, algo=F.FAIRY_ALGO_AUTO, workspace=False):
+    """workspace (GEMM only): pass the optional K-split workspace, filled with
+    0xFF bytes (NaNs if read before written)."""
     t = torch()
     n, m = layer.n, layer.m
     y_re = t.empty((B, n), dtype=t.float32, device="cuda")
@@ -94,7 +96,11 @@ def run_gemv(layer, x_re, x_im, xdtype, B, want_acc=False, gemm=False, algo=F.FA
     acc = t.empty((layer.planes, 4, B, n), dtype=t.int32, device="cuda") if want_acc else None
     ldx = x_re.shape[-1]
     if gemm:
-        F.fairy_cgemm(layer.desc, x_re, x_im, xdtype, B, ldx, y_re, y_im, n, acc, algo)
+        ws, wsb = None, 0
+        if workspace:
+            wsb = F.fairy_cgemm_workspace_bytes(layer.desc, B, xdtype, algo)
+            ws = t.full((max(wsb, 16),), 255, dtype=t.uint8, device="cuda")
+        F.fairy_cgemm(layer.desc, x_re, x_im, xdtype, B, ldx, y_re, y_im, n, acc, algo, ws, wsb)
     else:
         F.fairy_cgemv(layer.desc, x_re, x_im, xdtype, B, ldx, y_re, y_im, n, acc)
     t.cuda.synchronize()

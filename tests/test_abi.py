@@ -78,6 +78,33 @@ def test_workspace_sizes():
     assert F.fairy_phasequant_workspace_bytes(1 << 32, 1) == 0
 
 
+def test_cgemm_workspace_sizes():
+    """The matrix-core GEMM asks for a K-split workspace only where its
+    64-row x 64-token blocks would leave CUs idle: splits x 2 x M x n floats."""
+    L = F.make_clinear(2048, 2048, 2, 1, A, A)                   # P = 4: 32 row blocks
+    ws = lambda M, dt, algo: F.fairy_cgemm_workspace_bytes(L, M, dt, algo)
+    # bf16: 16 chunks of 128 columns; 32 blocks -> 8 splits of 2 chunks
+    assert ws(16, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA) == 8 * 2 * 16 * 2048 * 4
+    assert ws(64, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA) == 8 * 2 * 64 * 2048 * 4
+    # int8: 8 chunks of 256 columns -> 8 splits of 1
+    assert ws(64, F.FAIRY_I8, F.FAIRY_ALGO_MFMA) == 8 * 2 * 64 * 2048 * 4
+    # 3 token blocks -> 96 blocks -> 3 splits of 6 chunks (bf16)
+    assert ws(150, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA) == 3 * 2 * 150 * 2048 * 4
+    # enough blocks, the VALU path, AUTO below its matrix-core threshold, fp32: none
+    assert ws(256, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA) == 0          # 128 blocks
+    assert ws(2048, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA) == 0
+    assert ws(16, F.FAIRY_BF16, F.FAIRY_ALGO_VALU) == 0
+    assert ws(16, F.FAIRY_BF16, F.FAIRY_ALGO_AUTO) == 0
+    assert ws(32, F.FAIRY_BF16, F.FAIRY_ALGO_AUTO) == 8 * 2 * 32 * 2048 * 4
+    assert ws(64, F.FAIRY_F32, F.FAIRY_ALGO_MFMA) == 0
+    # plane counts that need several passes: none
+    assert F.fairy_cgemm_workspace_bytes(F.make_clinear(2048, 2048, 3, 1, A, A), 16, F.FAIRY_BF16,
+                                         F.FAIRY_ALGO_MFMA) == 0
+    # a short row (one chunk) cannot be split
+    assert F.fairy_cgemm_workspace_bytes(F.make_clinear(64, 128, 1, 0, A, A), 8, F.FAIRY_BF16,
+                                         F.FAIRY_ALGO_MFMA) == 0
+
+
 def status_of(fn, *args):
     return fn(*args)
 

@@ -264,6 +264,60 @@ def test_gemm_i8_exact(S, hc, n, m, M, algo):
     assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
 
 
+# K split of the matrix-core GEMM at token counts that leave CUs idle
+SPLIT_CASES = [
+    # (S, has_conj, n, m, M, xdtype)
+    (2, True, 2048, 2048, 16, F.FAIRY_BF16),    # the decode-batch case: 8 splits of 2 chunks
+    (2, True, 2048, 2048, 64, F.FAIRY_I8),      # 8 splits of 1 chunk
+    (1, False, 200, 1088, 5, F.FAIRY_BF16),     # P = 1, ragged rows and a half-full last chunk
+    (1, True, 130, 2064, 33, F.FAIRY_I8),       # P = 2, 33 groups: a one-group last chunk
+    (2, True, 5504, 2048, 8, F.FAIRY_BF16),     # 86 row blocks: 3 splits of 6, 6, 4 chunks
+    (2, True, 300, 4096, 150, F.FAIRY_BF16),    # 3 token blocks, ragged tokens
+]
+
+
+@pytest.mark.parametrize("S,hc,n,m,M,xdtype", SPLIT_CASES)
+def test_gemm_mfma_split_k(S, hc, n, m, M, xdtype):
+    log(f"gemm split-K dt={xdtype} S={S} conj={hc} n={n} m={m} M={M}")
+    P = S * (2 if hc else 1)
+    codes = synth.random_codes((P, n, m), 5 * n + m + M)
+    scales = synth.random_scales(P, n + 3 * M)
+    layer = layer_from_codes(codes, scales, S, hc)
+    assert F.fairy_cgemm_workspace_bytes(layer.desc, M, xdtype, F.FAIRY_ALGO_MFMA) > 0
+    if xdtype == F.FAIRY_BF16:
+        rb, ib, xr, xi = x_bf16(M, m, 23 + M)
+        args = (dev(rb), dev(ib))
+    else:
+        xr, xi = synth.int8_uniform((M, m), 29 + M)
+        args = (dev(xr), dev(xi))
+        xr, xi = xr.astype(np.float64), xi.astype(np.float64)
+    yr, yi, _ = run_gemv(layer, *args, xdtype, M, gemm=True, algo=F.FAIRY_ALGO_MFMA, workspace=True)
+    wr, wi = oracle.cgemv_dense(codes, scales, S, hc, xr, xi)
+    err = rel_l2(yr + 1j * yi, wr + 1j * wi)
+    log(f"  rel_l2={err:.3e}")
+    assert err <= TOL
+    # the unsplit launch (no workspace) agrees within the same bound
+    ur, ui, _ = run_gemv(layer, *args, xdtype, M, gemm=True, algo=F.FAIRY_ALGO_MFMA)
+    assert rel_l2(ur + 1j * ui, wr + 1j * wi) <= TOL
+    # and the split launch repeats bit for bit
+    zr, zi, _ = run_gemv(layer, *args, xdtype, M, gemm=True, algo=F.FAIRY_ALGO_MFMA, workspace=True)
+    assert np.array_equal(yr, zr) and np.array_equal(yi, zi)
+
+
+def test_gemm_mfma_split_k_with_acc_runs_unsplit():
+    """Raw int8 accumulators are exact per plane, so with acc requested the
+    call ignores the workspace and runs unsplit."""
+    codes = synth.random_codes((4, 256, 2048), 31)
+    scales = synth.random_scales(4, 32)
+    layer = layer_from_codes(codes, scales, 2, True)
+    xr, xi = synth.int8_uniform((16, 2048), 33)
+    yr, yi, acc = run_gemv(layer, dev(xr), dev(xi), F.FAIRY_I8, 16, want_acc=True, gemm=True,
+                           algo=F.FAIRY_ALGO_MFMA, workspace=True)
+    assert np.array_equal(acc.astype(np.int64), oracle.cgemv_acc_i64(codes, xr, xi))
+    wr, wi = oracle.cgemv_dense(codes, scales, 2, True, xr.astype(np.float64), xi.astype(np.float64))
+    assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
+
+
 def test_gemm_mfma_deterministic():
     codes = synth.random_codes((4, 256, 512), 8)
     layer = layer_from_codes(codes, synth.random_scales(4, 9), 2, True)
