@@ -241,9 +241,10 @@ fairy_status fairy_cgemm(const fairy_clinear* L, const void* x_re, const void* x
     if (M < 1 || M > kMaxDim) return FAIRY_ERR_INVALID_ARG;
     if (algo != FAIRY_ALGO_AUTO && algo != FAIRY_ALGO_VALU && algo != FAIRY_ALGO_MFMA) return FAIRY_ERR_INVALID_ARG;
     fairy::LayerArgs la;
-    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, &la);
+    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, &la, false);
     if (st != FAIRY_OK) return st;
     if (algo == FAIRY_ALGO_MFMA && xdtype == FAIRY_F32) return FAIRY_ERR_UNSUPPORTED;
+    if (!fairy::cgemm_uses_mfma(M, xdtype, algo) && L->m > max_m_for(xdtype)) return FAIRY_ERR_UNSUPPORTED;
     // the workspace is optional: without one the call runs unsplit
     const size_t need = fairy::cgemm_workspace_bytes(la, M, xdtype, algo);
     if (workspace && need && (workspace_bytes < need || !aligned(workspace, 16))) return FAIRY_ERR_WORKSPACE;
@@ -287,9 +288,10 @@ fairy_status fairy_cgemm_rope(const fairy_clinear* L, const void* x_re, const vo
     if (M < 1 || M > kMaxDim) return FAIRY_ERR_INVALID_ARG;
     if (algo != FAIRY_ALGO_AUTO && algo != FAIRY_ALGO_VALU && algo != FAIRY_ALGO_MFMA) return FAIRY_ERR_INVALID_ARG;
     fairy::LayerArgs la;
-    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, nullptr, &la);
+    fairy_status st = check_layer_call(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, nullptr, &la, false);
     if (st != FAIRY_OK) return st;
     if (algo == FAIRY_ALGO_MFMA && xdtype == FAIRY_F32) return FAIRY_ERR_UNSUPPORTED;
+    if (!fairy::cgemm_uses_mfma(M, xdtype, algo) && L->m > max_m_for(xdtype)) return FAIRY_ERR_UNSUPPORTED;
     if ((st = check_rope(positions, head_dim, base, &la)) != FAIRY_OK) return st;
     clear_stale_error();
     hipError_t e = fairy::launch_cgemm(la, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, nullptr, algo, nullptr,

@@ -6,7 +6,7 @@
 
 namespace fairy {
 
-static bool uses_mfma(int64_t M, int32_t xdtype, int32_t algo)
+bool cgemm_uses_mfma(int64_t M, int32_t xdtype, int32_t algo)
 {
     const bool mfma_ok = xdtype == FAIRY_BF16 || xdtype == FAIRY_I8;
     return (algo == FAIRY_ALGO_MFMA) || (algo == FAIRY_ALGO_AUTO && mfma_ok && M >= 32);
@@ -16,7 +16,7 @@ static bool uses_mfma(int64_t M, int32_t xdtype, int32_t algo)
 // keeps the partial sums here; every other path needs none.
 size_t cgemm_workspace_bytes(const LayerArgs& L, int64_t M, int32_t xdtype, int32_t algo)
 {
-    if (!uses_mfma(M, xdtype, algo) || (xdtype != FAIRY_BF16 && xdtype != FAIRY_I8)) return 0;
+    if (!cgemm_uses_mfma(M, xdtype, algo) || (xdtype != FAIRY_BF16 && xdtype != FAIRY_I8)) return 0;
     return cgemm_mfma_workspace_bytes(L.n, L.m, M, L.planes, xdtype);
 }
 
@@ -24,7 +24,7 @@ hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, 
                         int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc, int32_t algo,
                         void* workspace, hipStream_t s)
 {
-    if (uses_mfma(M, xdtype, algo)) {
+    if (cgemm_uses_mfma(M, xdtype, algo)) {
         if (xdtype != FAIRY_BF16 && xdtype != FAIRY_I8) return hipErrorNotSupported;
         const gemv::GemvArgs a = gemv::make_args(L, x_re, x_im, M, ldx, y_re, y_im, ldy, acc);
         return launch_cgemm_mfma(a, xdtype, workspace, s);

@@ -146,6 +146,10 @@ hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, 
                         int64_t batch, int64_t ldx, float* y_re, float* y_im, int64_t ldy,
                         int32_t* acc, hipStream_t s);
 
+// Whether fairy_cgemm takes the matrix-core path for these arguments (it
+// streams the activations in chunks, so any m; the VALU path stages whole
+// activation rows in LDS).
+bool cgemm_uses_mfma(int64_t M, int32_t xdtype, int32_t algo);
 size_t cgemm_workspace_bytes(const LayerArgs& L, int64_t M, int32_t xdtype, int32_t algo);
 hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, int32_t xdtype,
                         int64_t M, int64_t ldx, float* y_re, float* y_im, int64_t ldy, int32_t* acc,

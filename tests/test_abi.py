@@ -200,6 +200,12 @@ def test_cgemm_validation():
     assert f(*args(algo=3)) == F.FAIRY_ERR_INVALID_ARG
     assert f(*args(acc=A)) == F.FAIRY_ERR_INVALID_ARG
     assert f(*args(dt=F.FAIRY_F32, algo=F.FAIRY_ALGO_MFMA)) == F.FAIRY_ERR_UNSUPPORTED
+    # beyond the staged-activation width: unsupported on the VALU path (and
+    # on AUTO below its matrix-core threshold); the matrix-core path streams
+    Lw = layer(m=16384)
+    wide = lambda M, algo: f(ctypes.byref(Lw), A, A, F.FAIRY_BF16, M, 16384, A, A, 64, None, algo, None, 0, None)
+    assert wide(8, F.FAIRY_ALGO_VALU) == F.FAIRY_ERR_UNSUPPORTED
+    assert wide(8, F.FAIRY_ALGO_AUTO) == F.FAIRY_ERR_UNSUPPORTED
 
 
 def test_cgemv_lut_validation():

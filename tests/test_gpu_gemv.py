@@ -304,6 +304,28 @@ def test_gemm_mfma_split_k(S, hc, n, m, M, xdtype):
     assert np.array_equal(yr, zr) and np.array_equal(yi, zi)
 
 
+@pytest.mark.parametrize("xdtype,m", [(F.FAIRY_BF16, 16384), (F.FAIRY_I8, 28672)])
+def test_gemm_mfma_beyond_gemv_width(xdtype, m):
+    """The matrix-core GEMM streams activations in chunks, so it takes rows
+    wider than the GEMV can stage (14528 bf16, 26112 int8 columns)."""
+    n, M = 96, 40
+    codes = synth.random_codes((2, n, m), 41)
+    scales = synth.random_scales(2, 42)
+    layer = layer_from_codes(codes, scales, 1, True)
+    if xdtype == F.FAIRY_BF16:
+        rb, ib, xr, xi = x_bf16(M, m, 43)
+        args = (dev(rb), dev(ib))
+    else:
+        xr, xi = synth.int8_uniform((M, m), 44)
+        args = (dev(xr), dev(xi))
+    yr, yi, acc = run_gemv(layer, *args, xdtype, M, want_acc=xdtype == F.FAIRY_I8, gemm=True,
+                           algo=F.FAIRY_ALGO_MFMA)
+    wr, wi = oracle.cgemv_dense(codes, scales, 1, True, np.asarray(xr, np.float64), np.asarray(xi, np.float64))
+    assert rel_l2(yr + 1j * yi, wr + 1j * wi) <= TOL
+    if xdtype == F.FAIRY_I8:
+        assert np.array_equal(acc.astype(np.int64), oracle.cgemv_acc_i64(codes, xr, xi))
+
+
 def test_gemm_mfma_split_k_with_acc_runs_unsplit():
     """Raw int8 accumulators are exact per plane, so with acc requested the
     call ignores the workspace and runs unsplit."""
