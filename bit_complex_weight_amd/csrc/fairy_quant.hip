@@ -130,7 +130,7 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t count)
 // the stage's workspace (integer atomics: exact and order-independent; the
 // copies keep the blocks of a launch from contending on ~40 hot addresses).
 constexpr int kCopies = 2;
-constexpr int kGlobalCopies = 64;
+constexpr int kGlobalCopies = 16;
 constexpr int kStageBlocks = 1024;
 
 template <int V>

@@ -126,8 +126,8 @@ fairy_status fairy_real_to_complex(const float* R, int64_t n, int64_t m,
                                    float* u_re, float* u_im, float* w_re, float* w_im,
                                    void* stream);
 
-/* Workspace for fairy_phasequant: per stage, 64 copies of 512 uint64
- * exponent buckets plus 2 counts (263,168 bytes per stage; the copies spread
+/* Workspace for fairy_phasequant: per stage, 16 copies of 512 uint64
+ * exponent buckets plus 2 counts (65,792 bytes per stage; the copies spread
  * the integer atomics of the launch).  Returns 0 for invalid arguments. */
 size_t fairy_phasequant_workspace_bytes(int64_t count, int32_t stages);
 

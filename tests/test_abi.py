@@ -72,7 +72,7 @@ def test_packed_words():
 
 
 def test_workspace_sizes():
-    assert F.fairy_phasequant_workspace_bytes(1000, 2) == 2 * 64 * 514 * 8
+    assert F.fairy_phasequant_workspace_bytes(1000, 2) == 2 * 16 * 514 * 8
     assert F.fairy_phasequant_workspace_bytes(0, 2) == 0
     assert F.fairy_phasequant_workspace_bytes(10, 9) == 0
     assert F.fairy_phasequant_workspace_bytes(1 << 32, 1) == 0

@@ -77,9 +77,9 @@ def test_read_info_truncated():
 
 
 def test_quantize_workspace_bytes():
-    # real: 4 fp32 planes + 2S code planes + S x 64 copies of 514 uint64, each 256-aligned
+    # real: 4 fp32 planes + 2S code planes + S x 16 copies of 514 uint64, each 256-aligned
     n, m, S = 2048, 2048, 2
-    pq = S * 64 * 514 * 8
+    pq = S * 16 * 514 * 8
     want = 4 * n * m * 4 + 2 * S * n * m + ((pq + 255) // 256) * 256
     assert F.fairy_quantize_workspace_bytes(n, m, S, 1) == want
     assert F.fairy_quantize_workspace_bytes(n, m, S, 0) == S * n * m + ((pq + 255) // 256) * 256
