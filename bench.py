@@ -309,7 +309,7 @@ def main():
     if not (torch.equal(y_re, eager_y[0]) and torch.equal(y_im, eager_y[1])):
         raise SystemExit("graph replay output differs from the eager GEMV output")
     gbs = packed_bytes / (ms * 1e-3) / 1e9
-    # this box's streaming ceiling: a 256 MiB device copy (bytes read + written)
+    # the device's streaming ceiling: a 256 MiB device copy (bytes read + written)
     csrc = torch.empty((64 << 20,), dtype=torch.int32, device="cuda")
     cdst = torch.empty_like(csrc)
     cdst.copy_(csrc)
