@@ -143,26 +143,51 @@ __device__ __forceinline__ void read_frags(const uint8_t* xb, int ks, int q, int
 struct CodeRows {
     const uint32_t* base[kRT];
     bool ok[kRT];
-    int G, gstride;
-    __device__ __forceinline__ CodeRows(const GemvArgs& a, int row, int p, int q)
+    int G, gstride, q;
+    __device__ __forceinline__ CodeRows(const GemvArgs& a, int row, int p, int q_)
     {
         G = a.G;
         gstride = a.P * 4;
+        q = q_;
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
             const int r = row + 16 * rt;
             ok[rt] = r < a.n;
-            base[rt] = a.packed + ((int64_t)(ok[rt] ? r : 0) * G * a.P + p) * 4 + q;
+            base[rt] = a.packed + ((int64_t)(ok[rt] ? r : 0) * G * a.P + p) * 4;  // the (row, group 0, plane) unit
         }
     }
     template <int NG>
     __device__ __forceinline__ void chunk(int g0, uint32_t (&w)[kRT][NG]) const
     {
+        if constexpr (NG == 4) {
+            // Four groups, four lane quarters: quarter q loads the whole
+            // 16-byte unit of group g0 + q, and a 4x4 transpose across the
+            // quarters (two row-swap stages) gives quarter q word q of each
+            // group: one 128-bit load per row tile instead of four 32-bit ones.
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
+            for (int rt = 0; rt < kRT; ++rt) {
+                const uint4 u = (ok[rt] && g0 + q < G)
+                                    ? *reinterpret_cast<const uint4*>(base[rt] + (int64_t)(g0 + q) * gstride)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+                // quarters q, q ^ 2: the upper pair takes the lower pair's
+                // words 2, 3 in exchange for its words 0, 1
+                const auto a02 = __builtin_amdgcn_permlane32_swap(u.x, u.z, false, false);
+                const auto a13 = __builtin_amdgcn_permlane32_swap(u.y, u.w, false, false);
+                // quarters q, q ^ 1
+                const auto b01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+                const auto b23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
+                w[rt][0] = b01[0];
+                w[rt][1] = b01[1];
+                w[rt][2] = b23[0];
+                w[rt][3] = b23[1];
+            }
+        } else {
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi)
-                w[rt][gi] = (ok[rt] && g0 + gi < G) ? base[rt][(g0 + gi) * gstride] : 0u;
+            for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi)
+                    w[rt][gi] = (ok[rt] && g0 + gi < G) ? base[rt][(int64_t)(g0 + gi) * gstride + q] : 0u;
+        }
     }
 };
 
