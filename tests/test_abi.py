@@ -206,6 +206,14 @@ def test_cgemm_validation():
     wide = lambda M, algo: f(ctypes.byref(Lw), A, A, F.FAIRY_BF16, M, 16384, A, A, 64, None, algo, None, 0, None)
     assert wide(8, F.FAIRY_ALGO_VALU) == F.FAIRY_ERR_UNSUPPORTED
     assert wide(8, F.FAIRY_ALGO_AUTO) == F.FAIRY_ERR_UNSUPPORTED
+    # the optional K-split workspace: a given one must be large enough and aligned
+    Lb = layer(n=2048, m=2048)
+    need = F.fairy_cgemm_workspace_bytes(Lb, 16, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA)
+    assert need > 0
+    split = lambda w, wb: f(ctypes.byref(Lb), A, A, F.FAIRY_BF16, 16, 2048, A, A, 2048, None, F.FAIRY_ALGO_MFMA, w, wb,
+                            None)
+    assert split(A, need - 1) == F.FAIRY_ERR_WORKSPACE
+    assert split(A + 4, need) == F.FAIRY_ERR_WORKSPACE
 
 
 def test_cgemv_lut_validation():
