@@ -191,15 +191,16 @@ def attention_entry(ms, h, sq, sk, d, causal):
     """Useful work: scores 4 sq sk d (the real-equivalent dot products over 2d)
     plus the weighted sums 4 sq sk d (re and im); causal keeps the visible
     (query, key) pairs.  Matrix-core work of the kernel: 12 sq sk d per
-    processed 64-key chunk (the weights go through two bf16 MFMAs)."""
+    processed key chunk (the weights go through two bf16 MFMAs)."""
+    kc = 128 if d <= 64 else 64  # keys per staged chunk
     if causal:
         pairs = sum(min(sk, i + (sk - sq) + 1) for i in range(sq))
-        # a block of 128 queries walks the 64-key chunks up to its last query's diagonal
-        mfma_pairs = sum(((min(sk, qb * 128 + 128 + (sk - sq)) + 63) // 64) * 64 * 128
+        # a block of 128 queries walks the key chunks up to its last query's diagonal
+        mfma_pairs = sum(((min(sk, qb * 128 + 128 + (sk - sq)) + kc - 1) // kc) * kc * 128
                          for qb in range((sq + 127) // 128))
     else:
         pairs = sq * sk
-        mfma_pairs = ((sq + 127) // 128) * 128 * ((sk + 63) // 64) * 64
+        mfma_pairs = ((sq + 127) // 128) * 128 * ((sk + kc - 1) // kc) * kc
     alg = 8.0 * h * pairs * d
     mf = 12.0 * h * mfma_pairs * d
     t = ms * 1e-3

@@ -9,7 +9,8 @@
 //
 // One pass, online softmax (FlashAttention style).  A block is 8 waves over
 // 128 queries of one head (each staged key chunk serves 128 queries); each
-// wave owns 16 queries and walks the keys in chunks of 64, staged in LDS
+// wave owns 16 queries and walks the keys in chunks (128 keys for d <= 64,
+// 64 for d = 128, whose rows fill the registers and LDS), staged in LDS
 // through two buffers (keys as [key][re | im], values as [re/im][key][d],
 // both copied as they are in memory) and software-pipelined: the score
 // MFMAs of chunk i+1 are issued among the softmax arithmetic of chunk i.
@@ -31,8 +32,8 @@
 //  * O^T accumulates in fp32: lane l holds query l % 16 and four consecutive
 //    d, so the rescaling by the running maximum is per lane and the store is
 //    a float4 per lane.
-// Measured on MI355X (32 heads x 2048 tokens, d = 64, bf16): 0.082 ms causal,
-// 0.145 ms full.
+// Measured on MI355X (32 heads x 2048 tokens, d = 64, bf16): 0.079 ms causal,
+// 0.141 ms full.
 #include <type_traits>
 
 #include "fairy_internal.h"
@@ -46,7 +47,6 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQBlock = 16 * kWaves;  // queries per block
-constexpr int kKeys = 64;             // keys per chunk
 
 struct Args {
     const uint16_t *q_re, *q_im, *k_re, *k_im, *v_re, *v_im;
@@ -79,6 +79,9 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* p)
 
 template <int D>
 struct Geometry {
+    // keys per chunk: 128 halves the per-chunk costs (barrier, maximum,
+    // staging) where two buffers of them fit in LDS
+    static constexpr int kKeys = D <= 64 ? 128 : 64;
     static constexpr int D2 = 2 * D;              // length of the concatenated [re | im] vector
     static constexpr int kRowK = D2 * 2 + 16;     // bytes per staged key row (+ pad: conflict-free reads)
     // bytes per staged value row ([key][d], natural order): 32 more than the
@@ -145,6 +148,8 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
     constexpr int kRowV = Geometry<D>::kRowV;
     constexpr int kBytesK = Geometry<D>::kBytesK;
     constexpr int kBytesV = Geometry<D>::kBytesV;
+    constexpr int kKeys = Geometry<D>::kKeys;
+    constexpr int KT = kKeys / 16, KSP = kKeys / 32;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -254,16 +259,16 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
     };
     // S^T tiles of the chunk in buffer buf: st[kt][v] = unscaled score of
     // (key 16kt + 4g + v of the chunk, query qi)
-    auto scores = [&](int buf, floatx4_t(&st)[4]) {
+    auto scores = [&](int buf, floatx4_t(&st)[KT]) {
         const uint8_t* kb = s_k + buf * kBytesK;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) st[kt] = floatx4_t{0, 0, 0, 0};
+        for (int kt = 0; kt < KT; ++kt) st[kt] = floatx4_t{0, 0, 0, 0};
         // K-step outer, key tile inner: consecutive MFMAs use different
         // accumulators (a dependent MFMA waits for its predecessor's result)
 #pragma unroll
         for (int t = 0; t < KS; ++t)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
+            for (int kt = 0; kt < KT; ++kt) {
                 const bf16x8_t kf =
                     *reinterpret_cast<const bf16x8_t*>(kb + (kt * 16 + c16) * kRowK + (32 * t + 8 * g) * 2);
                 st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t], st[kt], 0, 0, 0);
@@ -272,7 +277,7 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
 
     // Scores of the chunk whose softmax comes next: unscaled (masked =
     // false) or scaled with the invisible keys at -inf (masked = true).
-    floatx4_t st[4];
+    floatx4_t st[KT];
     bool masked = false;
     // Maximum of the chunk in st, after masking it when the chunk runs past
     // the keys or (causal) past the diagonal of the wave's first query.
@@ -289,7 +294,7 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
             if (a.causal && qi + diag + 1 - k0 < lim64) lim64 = qi + diag + 1 - k0;
             const int lim = (int)(lim64 < 0 ? 0 : lim64 > kKeys ? kKeys : lim64);
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     st[kt][v] = (16 * kt + 4 * g + v < lim) ? scale2 * st[kt][v] : -INFINITY;
@@ -297,7 +302,7 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
                 }
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) mx = fmaxf(mx, st[kt][v]);
             mx *= scale2;  // scale2 >= 0: the maximum of the scaled scores
@@ -319,14 +324,14 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
         if (i + 2 < nch) load_k(k0 + 2 * kKeys);
         if (NEXT) load_v(k0 + kKeys);
 
-        floatx4_t sn[4];
+        floatx4_t sn[KT];
         if constexpr (NEXT) scores(buf, sn);
 
         // weights of chunk i against m_run: at most 2^kLazy
-        float p[4][4], ls = 0.0f;
+        float p[KT][4], ls = 0.0f;
         if (EDGE && masked) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     p[kt][v] = __builtin_amdgcn_exp2f(st[kt][v] - m_run);  // masked: 2^-inf = 0
@@ -334,7 +339,7 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
                 }
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     p[kt][v] = __builtin_amdgcn_exp2f(fmaf(st[kt][v], scale2, -m_run));
@@ -343,9 +348,9 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
         }
         l_run += ls;
         // P^T as bf16 hi + lo pairs, the B operands of the two K-steps
-        bf16x8_t ph[2], pl[2];
+        bf16x8_t ph[KSP], pl[KSP];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < KSP; ++ks) {
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -358,10 +363,10 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
             pl[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
         }
 
-        // O^T += V^T P^T, two K-steps of 32 keys
+        // O^T += V^T P^T, K-steps of 32 keys
         const uint8_t* vbuf = s_v + buf * kBytesV;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < KSP; ++ks) {
             // A operand of O^T: lane l needs V[key][16t + l % 16] for keys
             // 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3.  A transpose read
             // gives lane i of a 16-lane group element i % 4 of the 8 bytes
@@ -410,7 +415,7 @@ __device__ __forceinline__ void attend_tile(const Args& a, int64_t h, int64_t qb
             // settle the running maximum for chunk i+1: it is raised only
             // when some query of the wave exceeds it by more than kLazy
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) st[kt] = sn[kt];
+            for (int kt = 0; kt < KT; ++kt) st[kt] = sn[kt];
             const float mx = chunk_max(k0 + kKeys, edge_c);
             if (__ballot(mx > m_run + kLazy) != 0) {
                 const float m_new = fmaxf(m_run, mx);
