@@ -103,6 +103,28 @@ def test_cattention_llama_prefill_sampled_heads():
         assert err <= TOL
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_cattention_long_sequence_sampled(d):
+    """8192 tokens, causal: the first and last 64 queries against the oracle
+    (the first see keys 0..63 only; the last see all keys up to themselves,
+    so the oracle on those queries with every key reproduces them)."""
+    h, s = 2, 8192
+    log(f"cattention long sequence h={h} s={s} d={d}")
+    bits, v = make(h, s, s, d, 1000 + d)
+    scale = 1.0 / np.sqrt(2 * d)
+    o_re, o_im = run(bits, h, s, s, d, scale, 1)
+    q_re, q_im, k_re, k_im, v_re, v_im = v
+    w_re, w_im = oracle.cattention(q_re[:, :64], q_im[:, :64], k_re[:, :64], k_im[:, :64], v_re[:, :64],
+                                   v_im[:, :64], scale, True)
+    err = rel_l2(o_re[:, :64] + 1j * o_im[:, :64], w_re + 1j * w_im)
+    log(f"  first 64: rel_l2={err:.3e}")
+    assert err <= TOL
+    w_re, w_im = oracle.cattention(q_re[:, -64:], q_im[:, -64:], k_re, k_im, v_re, v_im, scale, True)
+    err = rel_l2(o_re[:, -64:] + 1j * o_im[:, -64:], w_re + 1j * w_im)
+    log(f"  last 64: rel_l2={err:.3e}")
+    assert err <= TOL
+
+
 def test_cattention_deterministic():
     h, sq, sk, d = 2, 100, 100, 64
     bits, _ = make(h, sq, sk, d, 5)
