@@ -11,7 +11,8 @@
 //   int8: v_perm ternary bytes (ternary_bytes),          v_mfma_i32_16x16x64_i8
 // and the activations are the MFMA A operand, staged in LDS.
 //
-// Waves are planes.  A block has 8 waves and covers 64 tokens; wave w works
+// Waves are planes.  A block has 8 waves and covers 64 tokens (16 or 32 when
+// the whole prompt is no longer: no matrix-core work on padding); wave w works
 // on plane plane0 + w % Q and on the 32 output rows of row group w / Q, over
 // the whole K range.  A plane's sums are therefore complete in registers
 // when the K loop ends (exact int32 for int8): the per-axis scales are
@@ -21,9 +22,10 @@
 // into y.  All waves of a block share the staged activations.
 //
 // Staging.  A chunk is 256 bytes of each token row (128 bf16 or 256 int8
-// columns), re and im, for the block's 64 tokens: 32 KiB, written straight
-// from global memory into LDS by global_load_lds_dwordx4 (a wave-instruction
-// fills 64 consecutive 16-byte slots, lane l slot l, from any addresses).
+// columns), re and im, for the block's 64 tokens: 32 KiB (8 KiB per 16
+// tokens), written straight from global memory into LDS by
+// global_load_lds_dwordx4 (a wave-instruction fills 64 consecutive 16-byte
+// slots, lane l slot l, from any addresses).
 // Two chunk buffers alternate: the next chunk streams in while the current
 // one is multiplied, one barrier per chunk.  Slot p of token row t holds
 // piece p ^ (t % 16) of the row, so the 16 rows a 16-lane phase reads sit on
@@ -56,23 +58,29 @@ typedef int intx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTT = 4;                  // 16-token tiles per wave
 constexpr int kRT = 2;                  // 16-row tiles per wave
-constexpr int kTok = 16 * kTT;          // tokens per block
 constexpr int kWaveRows = 16 * kRT;     // output rows per wave
 constexpr int kMaxGridY = 65535;
+constexpr int kRowBytes = 256;          // one token row of a chunk: 16 slots
+constexpr int kSteps = 4;               // K-steps per chunk
 
 template <int Q>
 constexpr int block_rows() { return (kWaves / Q) * kWaveRows; }
 
-constexpr int kRowBytes = 256;                          // one token row of a chunk: 16 slots
-constexpr int kBufBytes = 2 * kTok * kRowBytes;         // re and im: 32 KiB
-constexpr int kDmaInsts = kBufBytes / (64 * 16);        // wave-instructions per chunk
-constexpr int kSteps = 4;                               // K-steps per chunk
-// cross-wave sums: up to kWaves/2 writers x one component of a wave's tile
-constexpr int kRedBytes = (kWaves / 2) * kTT * kRT * 64 * 16;
-static_assert(kDmaInsts % kWaves == 0, "staging split");
-static_assert(2 * kBufBytes >= kRedBytes, "cross-wave sums reuse the chunk buffers");
+// TT 16-token tiles per wave (4 for long prompts; 1 or 2 when the whole
+// prompt is that short, so no matrix-core work goes to padding tokens)
+template <int TT>
+struct Tiles {
+    static constexpr int tok = 16 * TT;                     // tokens per block
+    static constexpr int buf_bytes = 2 * tok * kRowBytes;   // re and im: 8 KiB per token tile
+    static constexpr int dma_insts = buf_bytes / (64 * 16); // wave-instructions per chunk
+    // cross-wave sums: up to kWaves/2 writers x one component of a wave's tile
+    static constexpr int red_bytes = (kWaves / 2) * TT * kRT * 64 * 16;
+    static_assert(dma_insts % kWaves == 0, "staging split");
+    static_assert(2 * buf_bytes >= red_bytes, "cross-wave sums reuse the chunk buffers");
+};
+
+constexpr int token_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
 template <int XT>
 struct Geo {
@@ -88,16 +96,17 @@ struct Geo {
 // 16 zero bytes: the source of staging slots outside the matrix
 __device__ uint4 g_zero16;
 
-template <int XT>
+template <int XT, int TT>
 __device__ __forceinline__ void dma_chunk(const GemvArgs& a, int tok0, int c0, uint8_t* buf, int wave, int lane)
 {
     constexpr int es = Geo<XT>::esize;
+    constexpr int tok = Tiles<TT>::tok;
 #pragma unroll
-    for (int i = 0; i < kDmaInsts / kWaves; ++i) {
+    for (int i = 0; i < Tiles<TT>::dma_insts / kWaves; ++i) {
         const int wi = i * kWaves + wave;
         const int slot = wi * 64 + lane;
-        const int plane = slot / (kTok * 16);
-        const int t = (slot / 16) % kTok;
+        const int plane = slot / (tok * 16);
+        const int t = (slot / 16) % tok;
         const int piece = (slot % 16) ^ (t % 16);
         const int c = c0 + Geo<XT>::slot_cols * piece;
         const int tok = tok0 + t;
@@ -109,9 +118,10 @@ __device__ __forceinline__ void dma_chunk(const GemvArgs& a, int tok0, int c0, u
 }
 
 // byte offset of (re/im plane, token row t, 16-byte piece) in a chunk buffer
+template <int TT>
 __device__ __forceinline__ int slot_off(int plane, int t, int piece)
 {
-    return (plane * kTok + t) * kRowBytes + 16 * (piece ^ (t % 16));
+    return (plane * Tiles<TT>::tok + t) * kRowBytes + 16 * (piece ^ (t % 16));
 }
 
 // ternary_bytes order (byte b of register s is column i8_group_col(s, b))
@@ -124,17 +134,17 @@ __device__ __forceinline__ intx4_t to_natural_order(const uint32_t (&t)[4])
 }
 
 // A fragments of K-step ks for the lane (token rows 16tt + r16, quarter q)
-template <int XT>
+template <int XT, int TT>
 __device__ __forceinline__ void read_frags(const uint8_t* xb, int ks, int q, int r16,
-                                           typename Geo<XT>::Frag (&xr)[kTT], typename Geo<XT>::Frag (&xi)[kTT])
+                                           typename Geo<XT>::Frag (&xr)[TT], typename Geo<XT>::Frag (&xi)[TT])
 {
     using Frag = typename Geo<XT>::Frag;
     // bf16: columns 64(ks/2) + 16q + 8(ks%2) .. +8; int8: columns 64ks + 16q .. +16
     const int piece = (XT == FAIRY_BF16) ? 8 * (ks / 2) + 2 * q + ks % 2 : 4 * ks + q;
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
-        xr[tt] = *reinterpret_cast<const Frag*>(xb + slot_off(0, tt * 16 + r16, piece));
-        xi[tt] = *reinterpret_cast<const Frag*>(xb + slot_off(1, tt * 16 + r16, piece));
+    for (int tt = 0; tt < TT; ++tt) {
+        xr[tt] = *reinterpret_cast<const Frag*>(xb + slot_off<TT>(0, tt * 16 + r16, piece));
+        xi[tt] = *reinterpret_cast<const Frag*>(xb + slot_off<TT>(1, tt * 16 + r16, piece));
     }
 }
 
@@ -156,46 +166,77 @@ struct CodeRows {
             base[rt] = a.packed + ((int64_t)(ok[rt] ? r : 0) * G * a.P + p) * 4;  // the (row, group 0, plane) unit
         }
     }
+    // Raw loads of a chunk's words, taken apart by finish() once they have
+    // landed.  The loads are unconditional (no branch for the compiler to
+    // wait inside): a word outside the matrix or past this block's chunks
+    // (live = false) is read from 16 zero bytes instead.
     template <int NG>
-    __device__ __forceinline__ void chunk(int g0, uint32_t (&w)[kRT][NG]) const
+    struct Raw {
+        uint32_t v[kRT][4];
+    };
+    template <int NG>
+    __device__ __forceinline__ void load(int g0, Raw<NG>& r, bool live) const
     {
-        if constexpr (NG == 4) {
-            // Four groups, four lane quarters: quarter q loads the whole
-            // 16-byte unit of group g0 + q, and a 4x4 transpose across the
-            // quarters (two row-swap stages) gives quarter q word q of each
-            // group: one 128-bit load per row tile instead of four 32-bit ones.
+        const uint32_t* zero = reinterpret_cast<const uint32_t*>(&g_zero16);
 #pragma unroll
-            for (int rt = 0; rt < kRT; ++rt) {
-                const uint4 u = (ok[rt] && g0 + q < G)
-                                    ? *reinterpret_cast<const uint4*>(base[rt] + (int64_t)(g0 + q) * gstride)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-                // quarters q, q ^ 2: the upper pair takes the lower pair's
-                // words 2, 3 in exchange for its words 0, 1
-                const auto a02 = __builtin_amdgcn_permlane32_swap(u.x, u.z, false, false);
-                const auto a13 = __builtin_amdgcn_permlane32_swap(u.y, u.w, false, false);
-                // quarters q, q ^ 1
+        for (int rt = 0; rt < kRT; ++rt) {
+            if constexpr (NG == 4) {
+                // Four groups, four lane quarters: quarter q loads the whole
+                // 16-byte unit of group g0 + q (one 128-bit load per row tile
+                // instead of four 32-bit ones).
+                const bool on = live && ok[rt] && g0 + q < G;
+                const uint4 u = *reinterpret_cast<const uint4*>(on ? base[rt] + (int64_t)(g0 + q) * gstride : zero);
+                r.v[rt][0] = u.x;
+                r.v[rt][1] = u.y;
+                r.v[rt][2] = u.z;
+                r.v[rt][3] = u.w;
+            } else {
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    const bool on = live && ok[rt] && g0 + gi < G;
+                    r.v[rt][gi] = *(on ? base[rt] + (int64_t)(g0 + gi) * gstride + q : zero);
+                }
+            }
+        }
+    }
+    // word q of (row, group, plane) for each of the chunk's NG groups
+    template <int NG>
+    __device__ __forceinline__ static void finish(const Raw<NG>& r, uint32_t (&w)[kRT][NG])
+    {
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+            if constexpr (NG == 4) {
+                // 4x4 transpose across the quarters, two row-swap stages:
+                // quarters q, q ^ 2 (the upper pair takes the lower pair's
+                // words 2, 3 in exchange for its words 0, 1), then q, q ^ 1
+                const auto a02 = __builtin_amdgcn_permlane32_swap(r.v[rt][0], r.v[rt][2], false, false);
+                const auto a13 = __builtin_amdgcn_permlane32_swap(r.v[rt][1], r.v[rt][3], false, false);
                 const auto b01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
                 const auto b23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
                 w[rt][0] = b01[0];
                 w[rt][1] = b01[1];
                 w[rt][2] = b23[0];
                 w[rt][3] = b23[1];
+            } else {
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) w[rt][gi] = r.v[rt][gi];
             }
-        } else {
-#pragma unroll
-            for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-                for (int gi = 0; gi < NG; ++gi)
-                    w[rt][gi] = (ok[rt] && g0 + gi < G) ? base[rt][(int64_t)(g0 + gi) * gstride + q] : 0u;
         }
+    }
+    template <int NG>
+    __device__ __forceinline__ void chunk(int g0, uint32_t (&w)[kRT][NG], bool live = true) const
+    {
+        Raw<NG> r;
+        load<NG>(g0, r, live);
+        finish<NG>(r, w);
     }
 };
 
 // Epilogue: this wave's plane contribution from its four sums (int8: also
 // the raw sums to acc), the cross-wave sum of the Q planes of each row group
 // through LDS (red), and the store (or add) of y.
-template <int Q, typename Acc>
-__device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, const Acc (&acc)[4][kTT][kRT], int p,
+template <int Q, int TT, typename Acc>
+__device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, const Acc (&acc)[4][TT][kRT], int p,
                                             int slot, int rg, int row0, int tok0, int q, int r16, int lane,
                                             int accumulate, float* part)
 {
@@ -203,9 +244,9 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
     // y_im += s_re A3 + s_im A4; W planes multiply conj(x): A2 and A3 flip.
     const float s_re = a.scales[2 * p], s_im = a.scales[2 * p + 1];
     const float sg = (p < a.S) ? 1.0f : -1.0f;
-    floatx4_t pr[kTT][kRT], pi[kTT][kRT];
+    floatx4_t pr[TT][kRT], pi[TT][kRT];
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
             const int row = row0 + 16 * rt + r16;
@@ -245,20 +286,20 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
         for (int step = Q / 2; step >= 1; step /= 2) {
 #pragma unroll
             for (int comp = 0; comp < 2; ++comp) {
-                floatx4_t (&part)[kTT][kRT] = comp ? pi : pr;
+                floatx4_t (&part)[TT][kRT] = comp ? pi : pr;
                 __syncthreads();
                 if (slot >= step && slot < 2 * step) {
-                    floatx4_t* dst = red + (size_t)(rg * step + slot - step) * kTT * kRT * 64;
+                    floatx4_t* dst = red + (size_t)(rg * step + slot - step) * TT * kRT * 64;
 #pragma unroll
-                    for (int tt = 0; tt < kTT; ++tt)
+                    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
                         for (int rt = 0; rt < kRT; ++rt) dst[(tt * kRT + rt) * 64 + lane] = part[tt][rt];
                 }
                 __syncthreads();
                 if (slot < step) {
-                    const floatx4_t* src = red + (size_t)(rg * step + slot) * kTT * kRT * 64;
+                    const floatx4_t* src = red + (size_t)(rg * step + slot) * TT * kRT * 64;
 #pragma unroll
-                    for (int tt = 0; tt < kTT; ++tt)
+                    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
                         for (int rt = 0; rt < kRT; ++rt) part[tt][rt] += src[(tt * kRT + rt) * 64 + lane];
                 }
@@ -271,7 +312,7 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
         const int64_t mn = (int64_t)a.B * a.n;
         float* pre = part + (int64_t)blockIdx.z * 2 * mn;
 #pragma unroll
-        for (int tt = 0; tt < kTT; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt) {
                 const int row = row0 + 16 * rt + r16;
@@ -287,7 +328,7 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
         return;
     }
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
             const int row = row0 + 16 * rt + r16;
@@ -307,7 +348,7 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
         }
 }
 
-template <int XT, int Q>
+template <int XT, int Q, int TT>
 __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_base, int plane0, int accumulate,
                                                          int chunks_per_split, float* part)
 {
@@ -315,21 +356,22 @@ __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_bas
     using Frag = typename G_::Frag;
     using Acc = typename G_::Acc;
     constexpr int NG = G_::groups;
+    constexpr int kBufBytes = Tiles<TT>::buf_bytes;
     __shared__ __align__(16) uint8_t lds[2 * kBufBytes];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane >> 4, r16 = lane & 15;
     const int slot = wave % Q, rg = wave / Q;
     const int p = plane0 + slot;
     const int row0 = blockIdx.x * block_rows<Q>() + rg * kWaveRows;
-    const int tok0 = tok_base + blockIdx.y * kTok;
+    const int tok0 = tok_base + blockIdx.y * Tiles<TT>::tok;
     const int G = a.G;
     const CodeRows codes(a, row0 + r16, p, q);
 
-    Acc acc[4][kTT][kRT];
+    Acc acc[4][TT][kRT];
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int i = 0; i < kTT; ++i)
+        for (int i = 0; i < TT; ++i)
 #pragma unroll
             for (int j = 0; j < kRT; ++j) acc[b][i][j] = Acc{0, 0, 0, 0};
 
@@ -337,29 +379,18 @@ __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_bas
     const int nchunk = (G + NG - 1) / NG;
     const int ch0 = blockIdx.z * chunks_per_split;
     const int ch1 = (nchunk < ch0 + chunks_per_split) ? nchunk : ch0 + chunks_per_split;
-    dma_chunk<XT>(a, tok0, ch0 * G_::cols, lds, wave, lane);
-    uint32_t cw[kRT][NG];
-    codes.chunk(ch0 * NG, cw);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int ch = ch0; ch < ch1; ++ch) {
-        const int buf = (ch - ch0) & 1;
-        // the next chunk streams into the other buffer, which every wave
-        // finished reading before the barrier that ended the previous chunk
-        if (ch + 1 < ch1) dma_chunk<XT>(a, tok0, (ch + 1) * G_::cols, lds + (buf ^ 1) * kBufBytes, wave, lane);
-        uint32_t nw[kRT][NG];
-        codes.chunk((ch + 1) * NG, nw);
-        const uint8_t* xb = lds + buf * kBufBytes;
-        // A group past the end has zero activations and zero code words, so
-        // its products are exactly zero: the chunk needs no branch.
-        Frag xf[2][2][kTT];
-        read_frags<XT>(xb, 0, q, r16, xf[0][0], xf[0][1]);
+    // The products of one staged chunk (code words cw).  A group past the
+    // end has zero activations and zero code words, so its products are
+    // exactly zero: the chunk needs no branch.
+    uint32_t cw[kRT][NG], nw[kRT][NG];
+    auto products = [&](const uint8_t* xb) {
+        Frag xf[2][2][TT];
+        read_frags<XT, TT>(xb, 0, q, r16, xf[0][0], xf[0][1]);
 #pragma unroll
         for (int ks = 0; ks < kSteps; ++ks) {
-            if (ks + 1 < kSteps) read_frags<XT>(xb, ks + 1, q, r16, xf[(ks + 1) & 1][0], xf[(ks + 1) & 1][1]);
-            const Frag (&xr)[kTT] = xf[ks & 1][0];
-            const Frag (&xi)[kTT] = xf[ks & 1][1];
+            if (ks + 1 < kSteps) read_frags<XT, TT>(xb, ks + 1, q, r16, xf[(ks + 1) & 1][0], xf[(ks + 1) & 1][1]);
+            const Frag (&xr)[TT] = xf[ks & 1][0];
+            const Frag (&xi)[TT] = xf[ks & 1][1];
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt) {
                 if constexpr (XT == FAIRY_BF16) {
@@ -369,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_bas
                     const bf16x8_t re8 = __builtin_bit_cast(bf16x8_t, make_uint4(re2[0], re2[1], re2[2], re2[3]));
                     const bf16x8_t im8 = __builtin_bit_cast(bf16x8_t, make_uint4(im2[0], im2[1], im2[2], im2[3]));
 #pragma unroll
-                    for (int tt = 0; tt < kTT; ++tt) {
+                    for (int tt = 0; tt < TT; ++tt) {
                         acc[0][tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xr[tt], re8, acc[0][tt][rt], 0, 0, 0);
                         acc[1][tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xi[tt], im8, acc[1][tt][rt], 0, 0, 0);
                         acc[2][tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xi[tt], re8, acc[2][tt][rt], 0, 0, 0);
@@ -381,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_bas
                     const intx4_t re4 = to_natural_order(re);
                     const intx4_t im4 = to_natural_order(im);
 #pragma unroll
-                    for (int tt = 0; tt < kTT; ++tt) {
+                    for (int tt = 0; tt < TT; ++tt) {
                         acc[0][tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xr[tt], re4, acc[0][tt][rt], 0, 0, 0);
                         acc[1][tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi[tt], im4, acc[1][tt][rt], 0, 0, 0);
                         acc[2][tt][rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xi[tt], re4, acc[2][tt][rt], 0, 0, 0);
@@ -390,14 +421,65 @@ __global__ __launch_bounds__(kThreads) void k_cgemm_mfma(GemvArgs a, int tok_bas
                 }
             }
         }
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) cw[rt][gi] = nw[rt][gi];
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into the other buffer have landed
+    };
+    // The code words issued at the top of a chunk stay there (the scheduler
+    // would move them next to their use and wait for them inside the
+    // chunk); the int8 transpose of them stays after the products.
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+    if constexpr (XT == FAIRY_BF16 && TT == 4) {
+        // bf16, 64-token blocks: one chunk ahead.  Chunk ch + 1 streams into
+        // the other buffer, which every wave finished reading before the
+        // barrier that ended the previous chunk.  (The loop below measured
+        // 3% slower here.)
+        dma_chunk<XT, TT>(a, tok0, ch0 * G_::cols, lds, wave, lane);
+        codes.chunk(ch0 * NG, cw);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        for (int ch = ch0; ch < ch1; ++ch) {
+            const int buf = (ch - ch0) & 1;
+            if (ch + 1 < ch1) dma_chunk<XT, TT>(a, tok0, (ch + 1) * G_::cols, lds + (buf ^ 1) * kBufBytes, wave, lane);
+            CodeRows::Raw<NG> rn;
+            codes.load<NG>((ch + 1) * NG, rn, ch + 1 < ch1);
+            fence();
+            products(lds + buf * kBufBytes);
+            CodeRows::finish<NG>(rn, cw);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into the other buffer have landed
+            __syncthreads();
+        }
+    } else {
+        // Short prompts and int8.  A block of one or two chunks (a K split
+        // of a short prompt) loads both before its first barrier: one round
+        // of loads, not two.  A longer one waits for its first chunk only
+        // and streams the second under it.  Code words run two chunks ahead
+        // (cw, nw, then the raw words of chunk ch + 2).
+        const bool both = ch1 - ch0 <= 2;
+        dma_chunk<XT, TT>(a, tok0, ch0 * G_::cols, lds, wave, lane);
+        codes.chunk(ch0 * NG, cw);
+        codes.chunk((ch0 + 1) * NG, nw, ch0 + 1 < ch1);
+        if (both && ch0 + 1 < ch1) dma_chunk<XT, TT>(a, tok0, (ch0 + 1) * G_::cols, lds + kBufBytes, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (!both) dma_chunk<XT, TT>(a, tok0, (ch0 + 1) * G_::cols, lds + kBufBytes, wave, lane);
+        for (int ch = ch0; ch < ch1; ++ch) {
+            const int buf = (ch - ch0) & 1;
+            CodeRows::Raw<NG> rnn;
+            codes.load<NG>((ch + 2) * NG, rnn, ch + 2 < ch1);
+            fence();
+            products(lds + buf * kBufBytes);
+            if constexpr (NG == 4) fence();
+#pragma unroll
+            for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) cw[rt][gi] = nw[rt][gi];
+            CodeRows::finish<NG>(rnn, nw);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next chunk have landed
+            __syncthreads();                // and every wave is done with this buffer:
+            // chunk ch + 2 streams into it while chunk ch + 1 is multiplied
+            if (ch + 2 < ch1) dma_chunk<XT, TT>(a, tok0, (ch + 2) * G_::cols, lds + buf * kBufBytes, wave, lane);
+        }
     }
-    finish_tile<Q>(a, reinterpret_cast<floatx4_t*>(lds), acc, p, slot, rg, row0, tok0, q, r16, lane, accumulate,
+    finish_tile<Q, TT>(a, reinterpret_cast<floatx4_t*>(lds), acc, p, slot, rg, row0, tok0, q, r16, lane, accumulate,
                    part);
 }
 
@@ -410,9 +492,22 @@ __global__ __launch_bounds__(256) void k_split_sum(GemvArgs a, const float* part
     if (idx >= mn) return;
     const int tok = (int)(idx / a.n), row = (int)(idx % a.n);
     float sr = 0.0f, si = 0.0f;
-    for (int z = 0; z < splits; ++z) {
-        sr += part[2 * z * mn + idx];
-        si += part[(2 * z + 1) * mn + idx];
+    // eight splits' loads in flight at once (a split past the end re-reads
+    // the last one and is not added)
+    for (int z0 = 0; z0 < splits; z0 += 8) {
+        float vr[8], vi[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t z = (z0 + j < splits) ? z0 + j : splits - 1;
+            vr[j] = part[2 * z * mn + idx];
+            vi[j] = part[(2 * z + 1) * mn + idx];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (z0 + j < splits) {
+                sr += vr[j];
+                si += vi[j];
+            }
     }
     float* yr = a.y_re + (int64_t)tok * a.ldy + row;
     float* yi = a.y_im + (int64_t)tok * a.ldy + row;
@@ -435,7 +530,8 @@ int split_count(int64_t n, int64_t m, int64_t M, int P, int xdtype)
     if (P != 1 && P != 2 && P != 4) return 1;
     const int Q = P;
     const int64_t rows = (kWaves / Q) * kWaveRows;
-    const int64_t blocks = ((n + rows - 1) / rows) * ((M + kTok - 1) / kTok);
+    const int64_t tok = 16 * token_tiles(M);
+    const int64_t blocks = ((n + rows - 1) / rows) * ((M + tok - 1) / tok);
     const int64_t G = m / 64;
     const int ng = xdtype == FAIRY_BF16 ? chunk_groups<FAIRY_BF16>() : chunk_groups<FAIRY_I8>();
     const int64_t nchunk = (G + ng - 1) / ng;
@@ -447,15 +543,16 @@ int split_count(int64_t n, int64_t m, int64_t M, int P, int xdtype)
     return (int)((nchunk + cps - 1) / cps);
 }
 
-template <int XT, int Q>
+template <int XT, int Q, int TT>
 hipError_t launch_pass(const GemvArgs& a, int plane0, int accumulate, float* part, int splits, hipStream_t s)
 {
+    constexpr int kTok = Tiles<TT>::tok;
     const int64_t row_blocks = (a.n + block_rows<Q>() - 1) / block_rows<Q>();
     const int64_t tok_blocks = ((int64_t)a.B + kTok - 1) / kTok;
     const int nchunk = (a.G + Geo<XT>::groups - 1) / Geo<XT>::groups;
     if (part) {
         const int cps = (nchunk + splits - 1) / splits;
-        hipLaunchKernelGGL((k_cgemm_mfma<XT, Q>), dim3((unsigned)row_blocks, (unsigned)tok_blocks, (unsigned)splits),
+        hipLaunchKernelGGL((k_cgemm_mfma<XT, Q, TT>), dim3((unsigned)row_blocks, (unsigned)tok_blocks, (unsigned)splits),
                            dim3(kThreads), 0, s, a, 0, plane0, 0, cps, part);
         const int64_t mn = (int64_t)a.B * a.n;
         hipLaunchKernelGGL(k_split_sum, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, s, a, part, splits,
@@ -464,13 +561,13 @@ hipError_t launch_pass(const GemvArgs& a, int plane0, int accumulate, float* par
     }
     for (int64_t tb = 0; tb < tok_blocks; tb += kMaxGridY) {
         const int64_t nb = (tok_blocks - tb < kMaxGridY) ? tok_blocks - tb : kMaxGridY;
-        hipLaunchKernelGGL((k_cgemm_mfma<XT, Q>), dim3((unsigned)row_blocks, (unsigned)nb), dim3(kThreads), 0, s, a,
+        hipLaunchKernelGGL((k_cgemm_mfma<XT, Q, TT>), dim3((unsigned)row_blocks, (unsigned)nb), dim3(kThreads), 0, s, a,
                            (int)(tb * kTok), plane0, accumulate, nchunk, (float*)nullptr);
     }
     return hipGetLastError();
 }
 
-template <int XT>
+template <int XT, int TT>
 hipError_t launch_all(const GemvArgs& a, void* workspace, hipStream_t s)
 {
     // split K when a workspace is given, no raw accumulators are asked for,
@@ -478,9 +575,9 @@ hipError_t launch_all(const GemvArgs& a, void* workspace, hipStream_t s)
     const int splits = split_count(a.n, a.m, a.B, a.P, XT);
     if (workspace && !a.acc && splits > 1) {
         float* part = static_cast<float*>(workspace);
-        if (a.P == 4) return launch_pass<XT, 4>(a, 0, 0, part, splits, s);
-        if (a.P == 2) return launch_pass<XT, 2>(a, 0, 0, part, splits, s);
-        return launch_pass<XT, 1>(a, 0, 0, part, splits, s);
+        if (a.P == 4) return launch_pass<XT, 4, TT>(a, 0, 0, part, splits, s);
+        if (a.P == 2) return launch_pass<XT, 2, TT>(a, 0, 0, part, splits, s);
+        return launch_pass<XT, 1, TT>(a, 0, 0, part, splits, s);
     }
     hipError_t e = hipSuccess;
     for (int p0 = 0; p0 < a.P && e == hipSuccess;) {
@@ -489,9 +586,9 @@ hipError_t launch_all(const GemvArgs& a, void* workspace, hipStream_t s)
         const int q = rem >= 4 ? 4 : rem >= 2 ? 2 : 1;
         GemvArgs pass = a;
         if (p0 + q < a.P) pass.pos = nullptr;  // the rotation applies to the finished sum
-        if (q == 4) e = launch_pass<XT, 4>(pass, p0, acc, nullptr, 1, s);
-        else if (q == 2) e = launch_pass<XT, 2>(pass, p0, acc, nullptr, 1, s);
-        else e = launch_pass<XT, 1>(pass, p0, acc, nullptr, 1, s);
+        if (q == 4) e = launch_pass<XT, 4, TT>(pass, p0, acc, nullptr, 1, s);
+        else if (q == 2) e = launch_pass<XT, 2, TT>(pass, p0, acc, nullptr, 1, s);
+        else e = launch_pass<XT, 1, TT>(pass, p0, acc, nullptr, 1, s);
         p0 += q;
     }
     return e;
@@ -501,8 +598,15 @@ hipError_t launch_all(const GemvArgs& a, void* workspace, hipStream_t s)
 
 hipError_t launch_cgemm_mfma(const gemv::GemvArgs& a, int32_t xdtype, void* workspace, hipStream_t s)
 {
-    return (xdtype == FAIRY_BF16) ? mfma::launch_all<FAIRY_BF16>(a, workspace, s)
-                                  : mfma::launch_all<FAIRY_I8>(a, workspace, s);
+    using namespace mfma;
+    const int tt = token_tiles(a.B);
+    if (xdtype == FAIRY_BF16)
+        return tt == 1 ? launch_all<FAIRY_BF16, 1>(a, workspace, s)
+             : tt == 2 ? launch_all<FAIRY_BF16, 2>(a, workspace, s)
+                       : launch_all<FAIRY_BF16, 4>(a, workspace, s);
+    return tt == 1 ? launch_all<FAIRY_I8, 1>(a, workspace, s)
+         : tt == 2 ? launch_all<FAIRY_I8, 2>(a, workspace, s)
+                   : launch_all<FAIRY_I8, 4>(a, workspace, s);
 }
 
 size_t cgemm_mfma_workspace_bytes(int64_t n, int64_t m, int64_t M, int32_t P, int32_t xdtype)

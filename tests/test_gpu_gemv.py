@@ -232,6 +232,9 @@ GEMM_CASES = [
     (1, True, 130, 320, 65),       # P = 2
     (3, False, 50, 192, 70),       # P = 3: a 2-plane pass, then a 1-plane pass adding into y
     (7, False, 33, 64, 129),       # P = 7: 4 + 2 + 1 planes, three token blocks
+    (2, True, 70, 192, 24),        # 32-token blocks (17..32 tokens), ragged
+    (3, True, 100, 128, 17),       # 32-token blocks, P = 6: a 4-plane then a 2-plane pass
+    (7, False, 33, 64, 16),        # 16-token blocks, P = 7 in three passes
 ]
 
 
@@ -273,6 +276,8 @@ SPLIT_CASES = [
     (1, True, 130, 2064, 33, F.FAIRY_I8),       # P = 2, 33 groups: a one-group last chunk
     (2, True, 5504, 2048, 8, F.FAIRY_BF16),     # 86 row blocks: 3 splits of 6, 6, 4 chunks
     (2, True, 300, 4096, 150, F.FAIRY_BF16),    # 3 token blocks, ragged tokens
+    (2, True, 2048, 2048, 32, F.FAIRY_BF16),    # 32-token blocks: 8 splits of 2 chunks
+    (2, True, 1000, 2048, 20, F.FAIRY_I8),      # 32-token blocks, ragged rows and tokens
 ]
 
 
