@@ -27,7 +27,7 @@ int pick_bch(int xdtype, int B, int m64)
 int pick_bch_lp(int xdtype, int B, int m64)
 {
     int bch = B <= 1 ? 1 : B <= 4 ? 2 : 4;
-    while (bch > 1 && (size_t)x_bytes_per_col(xdtype, m64) * bch > 64 * 1024) bch /= 2;
+    while (bch > 1 && (size_t)x_bytes_per_col(xdtype, m64) * bch + 16 > 64 * 1024) bch /= 2;  // + spare slot
     return bch;
 }
 

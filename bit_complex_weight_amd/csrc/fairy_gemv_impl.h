@@ -96,6 +96,9 @@ __device__ __forceinline__ int x_col_off(int xdtype, int c)
     return (c >> 6) * x_group_bytes(xdtype) + (c & 63) * x_esize(xdtype);
 }
 
+// 16 zero bytes: what a load that is not needed reads instead of its address
+static __device__ uint4 g_zero_unit;
+
 // ---------------------------------------------------------------------------
 // Activation staging into LDS.  Per batch column b of the chunk:
 //   bf16: re plane [m64] then im plane [m64] (uint16)
@@ -317,29 +320,63 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
     const int G = a.G;
     const int b0 = blockIdx.y * BCH;
     const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
-    // unit (g, p) of the row is at g*P + p = lane + NL*k for g = gl + GS*k
+    // unit (g, p) of the row is at g*P + p = lane + NL*k for g = gl + GS*k.
+    // Every load below is unconditional: one that is not needed reads 16
+    // zero bytes instead (a load under a branch makes the compiler wait for
+    // it inside the branch, before anything else can run).
     const uint4* wl = reinterpret_cast<const uint4*>(a.packed) + ((int64_t)(row_ok ? row : 0) * G * P + lane);
+    const uint4* zero = &g_zero_unit;
+    const int pbytes = x_plane_bytes(XT, a.m64);
+    const int col_bytes = 2 * pbytes;
+    auto x_src = [&](int b, int pl, int c) -> const uint4* {
+        return (b < nb && c < a.m) ? reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pl ? a.x_im : a.x_re) +
+                                                                    ((int64_t)(b0 + b) * a.ldx + c) * esize)
+                                   : zero;
+    };
+    auto x_dst = [&](int b, int pl, int c) {
+        return reinterpret_cast<uint4*>(lds + (size_t)b * col_bytes + pl * pbytes + x_col_off(XT, c));
+    };
+    // The first activation columns are loaded first, then the code words,
+    // then the activations are stored: the stores wait for the activations
+    // (from L2) while the code words (from HBM) are still in flight.  The
+    // stores are unconditional too (one that is not needed goes to a spare
+    // 16-byte slot past the staged columns), so the compiler has no branch
+    // to sink the activation loads into.
+    const int c0 = threadIdx.x * per_elems;
+    uint4* spare = reinterpret_cast<uint4*>(lds + (size_t)BCH * col_bytes);
+    // (one vector value, not an array: an array live across the scheduling
+    // barrier is kept in scratch memory)
+    typedef uint32_t xvec_t __attribute__((ext_vector_type(8 * BCH)));
+    xvec_t xv;
+#pragma unroll
+    for (int i = 0; i < 2 * BCH; ++i) {
+        const uint4 v = *x_src(i >> 1, i & 1, c0);
+        xv[4 * i] = v.x;
+        xv[4 * i + 1] = v.y;
+        xv[4 * i + 2] = v.z;
+        xv[4 * i + 3] = v.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the code-word loads after these
     uint4 cur[2], nxt[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-        cur[u] = (row_ok && active && gl + u * GS < G) ? wl[NL * u] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 2; ++u) cur[u] = *((row_ok && active && gl + u * GS < G) ? wl + NL * u : zero);
+#pragma unroll
+    for (int i = 0; i < 2 * BCH; ++i)
+        *((c0 < a.m64 && (i >> 1) < nb) ? x_dst(i >> 1, i & 1, c0) : spare) =
+            make_uint4(xv[4 * i], xv[4 * i + 1], xv[4 * i + 2], xv[4 * i + 3]);
+    // rows longer than one pass of the block
+    for (int c = c0 + kThreadsLp * per_elems; c < a.m64; c += kThreadsLp * per_elems) {
+        uint4 v[2 * BCH];
+#pragma unroll
+        for (int i = 0; i < 2 * BCH; ++i) v[i] = *x_src(i >> 1, i & 1, c);
+#pragma unroll
+        for (int i = 0; i < 2 * BCH; ++i) {
+            if ((i >> 1) < nb) *x_dst(i >> 1, i & 1, c) = v[i];
+        }
+    }
     // decoded weights are +-2: half-scales; W planes multiply conj(x)
     const float hr = 0.5f * a.scales[2 * p], hi = 0.5f * a.scales[2 * p + 1];
     const float sg = (p < a.S) ? 1.0f : -1.0f;
-    const int pbytes = x_plane_bytes(XT, a.m64);
-    const int col_bytes = 2 * pbytes;
-    for (int b = 0; b < nb; ++b)
-#pragma unroll
-        for (int pl = 0; pl < 2; ++pl) {
-            const uint8_t* src =
-                reinterpret_cast<const uint8_t*>(pl ? a.x_im : a.x_re) + (int64_t)(b0 + b) * a.ldx * esize;
-            uint8_t* dst = lds + (size_t)b * col_bytes + pl * pbytes;
-            for (int c = threadIdx.x * per_elems; c < a.m64; c += kThreadsLp * per_elems) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (c < a.m) v = *reinterpret_cast<const uint4*>(src + (size_t)c * esize);
-                *reinterpret_cast<uint4*>(dst + x_col_off(XT, c)) = v;
-            }
-        }
     __syncthreads();
 
     float A[4][BCH];
@@ -352,8 +389,8 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
         const int gn = g0 + 2 * GS;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            nxt[u] = (row_ok && active && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + NL * u]
-                                                             : make_uint4(0, 0, 0, 0);
+            nxt[u] = *((row_ok && active && gn + u * GS < G) ? wl + (int64_t)(gn - gl) * P + NL * u : zero);
+        __builtin_amdgcn_sched_barrier(0);  // issued before these units' sums, not next to their use
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int g = g0 + u * GS;
@@ -535,7 +572,7 @@ template <int XT, int P, int BCH>
 hipError_t launch_lp_t(const GemvArgs& a, hipStream_t s)
 {
     const dim3 grid((a.n + (kThreadsLp / 64) - 1) / (kThreadsLp / 64), (a.B + BCH - 1) / BCH);
-    const size_t lds = (size_t)x_bytes_per_col(XT, a.m64) * BCH;
+    const size_t lds = (size_t)x_bytes_per_col(XT, a.m64) * BCH + 16;  // + the spare slot
     hipLaunchKernelGGL((k_cgemv_lp<XT, P, BCH>), grid, dim3(kThreadsLp), lds, s, a);
     return hipGetLastError();
 }
