@@ -73,14 +73,47 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp_i8(GemvArgs a)
     const int G = a.G;
     const int b0 = blockIdx.y * BCH;
     const int nb = (a.B - b0 < BCH) ? a.B - b0 : BCH;
-    // unit (g, p) of the row is at g*P + p = lane + 64k for g = gl + GS*k
+    // unit (g, p) of the row is at g*P + p = lane + 64k for g = gl + GS*k.
+    // Every load is unconditional: one that is not needed reads 16 zero
+    // bytes (a load under a branch makes the compiler wait for it inside the
+    // branch), and a store that is not needed goes to a spare LDS slot.
     const uint4* wl = reinterpret_cast<const uint4*>(a.packed) + ((int64_t)(row_ok ? row : 0) * G * P + lane);
+    const uint4* zero = &g_zero_unit;
+    const int pbytes = x_plane_bytes(FAIRY_I8, a.m64);
+    uint4* spare = reinterpret_cast<uint4*>(lds + (size_t)BCH * 2 * pbytes);
+    // staged activations: 16-byte pieces, per batch column re then im
+    const int per = a.m64 / 16;
+    const int pieces = nb * 2 * per;
+    auto piece = [&](int idx, const uint4*& src, uint4*& dst) {
+        const int b = idx / (2 * per);
+        const int rem = idx - b * 2 * per;
+        const int plane = rem / per;
+        const int c = (rem - plane * per) * 16;
+        const bool on = idx < pieces;
+        src = (on && c < a.m) ? reinterpret_cast<const uint4*>(reinterpret_cast<const int8_t*>(plane ? a.x_im : a.x_re) +
+                                                               (int64_t)(b0 + b) * a.ldx + c)
+                              : zero;
+        dst = on ? reinterpret_cast<uint4*>(lds + (size_t)(2 * b + plane) * pbytes + x_col_off(FAIRY_I8, c)) : spare;
+    };
+    // The first activation pieces are loaded, then the code words, then the
+    // pieces are stored: the stores wait for the activations (from L2) while
+    // the code words (from HBM) are still in flight.
+    const uint4* src0;
+    uint4* dst0;
+    piece(threadIdx.x, src0, dst0);
+    const uint4 x0 = *src0;
+    __builtin_amdgcn_sched_barrier(0);
     uint4 cur[2], nxt[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) cur[u] = (row_ok && gl + u * GS < G) ? wl[64 * u] : make_uint4(0, 0, 0, 0);
-    stage_x<FAIRY_I8>(a, b0, nb, lds);
+    for (int u = 0; u < 2; ++u) cur[u] = *((row_ok && gl + u * GS < G) ? wl + 64 * u : zero);
+    *dst0 = i8_reorder(x0);
+    for (int idx = threadIdx.x + kThreadsLp; idx < pieces; idx += kThreadsLp) {
+        const uint4* src;
+        uint4* dst;
+        piece(idx, src, dst);
+        *dst = i8_reorder(*src);
+    }
     __syncthreads();
-    const int pbytes = x_plane_bytes(FAIRY_I8, a.m64);
 
     int A[4][BCH];
 #pragma unroll
@@ -91,8 +124,8 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp_i8(GemvArgs a)
         // the next two units are in flight while these two are summed
         const int gn = g0 + 2 * GS;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-            nxt[u] = (row_ok && gn + u * GS < G) ? wl[(int64_t)(gn - gl) * P + 64 * u] : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) nxt[u] = *((row_ok && gn + u * GS < G) ? wl + (int64_t)(gn - gl) * P + 64 * u : zero);
+        __builtin_amdgcn_sched_barrier(0);  // issued before these units' sums, not next to their use
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int g = g0 + u * GS;
@@ -130,7 +163,7 @@ template <int P, int BCH>
 hipError_t launch_lp_i8_t(const GemvArgs& a, hipStream_t s)
 {
     const dim3 grid((a.n + (kThreadsLp / 64) - 1) / (kThreadsLp / 64), (a.B + BCH - 1) / BCH);
-    const size_t lds = (size_t)x_bytes_per_col(FAIRY_I8, a.m64) * BCH;
+    const size_t lds = (size_t)x_bytes_per_col(FAIRY_I8, a.m64) * BCH + 16;  // + the spare slot
     hipLaunchKernelGGL((k_cgemv_lp_i8<P, BCH>), grid, dim3(kThreadsLp), lds, s, a);
     return hipGetLastError();
 }

@@ -107,6 +107,25 @@ static __device__ uint4 g_zero_unit;
 //         reordered to the four dot4 groups (see i8_group_col).
 // Columns >= m are zero.
 // ---------------------------------------------------------------------------
+// int8 staging: the 16 bytes of a 16-column word reordered to the four dot4
+// groups (byte b of register s holds column i8_group_col(s, b))
+__device__ __forceinline__ uint4 i8_reorder(uint4 v)
+{
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int t = i8_group_col(s, bb);
+            o |= ((in[t >> 2] >> (8 * (t & 3))) & 0xFFu) << (8 * bb);
+        }
+        out[s] = o;
+    }
+    return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 template <int XT>
 __device__ __forceinline__ void stage_x(const GemvArgs& a, int b0, int nb, uint8_t* lds)
 {
@@ -124,21 +143,7 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, int b0, int nb, uint8
                              ((int64_t)(b0 + b) * a.ldx + c) * esize;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (c < a.m) v = *reinterpret_cast<const uint4*>(src);
-        if constexpr (XT == FAIRY_I8) {
-            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-            uint32_t out[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                uint32_t o = 0;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb) {
-                    const int t = i8_group_col(s, bb);
-                    o |= ((in[t >> 2] >> (8 * (t & 3))) & 0xFFu) << (8 * bb);
-                }
-                out[s] = o;
-            }
-            v = make_uint4(out[0], out[1], out[2], out[3]);
-        }
+        if constexpr (XT == FAIRY_I8) v = i8_reorder(v);
         *dst = v;
     }
 }
