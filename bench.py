@@ -42,7 +42,7 @@ GEMV_KERNEL = "k_cgemv_lp<bf16,P=4,BCH=1> (one row per wave, lane-fixed planes)"
 # HBM bytes per launch of GEMV_KERNEL on this workload, from the FETCH_SIZE and
 # WRITE_SIZE counters scaled by a plain copy's (profiles/gemv_lp_bf16_2048x2048_S2_B1.md);
 # None whenever the kernel has changed since those counters were taken
-GEMV_TRAFFIC_BYTES = 4377501
+GEMV_TRAFFIC_BYTES = 4380672
 POOL_BYTES = 512 << 20
 
 
