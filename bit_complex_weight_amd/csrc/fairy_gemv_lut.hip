@@ -60,30 +60,45 @@ __device__ __forceinline__ float load_x(const void* base, int c)
         return reinterpret_cast<const float*>(base)[c];
 }
 
-// Table k of the block (unit jj = k / 32 of the chunk, word u, nibble i).
+// 16 zero bytes: what a load that is not needed reads instead
+static __device__ uint4 g_lut_zero;
+
+// Inputs of table k of the block (unit j of the row, word u, nibble i): the
+// activations at the pair's two columns and the unit's plane scales.  Every
+// load is unconditional (a column past m reads zero bytes), so none of them
+// sits in a branch for the compiler to wait inside.
+struct TableIn {
+    float xr_lo, xi_lo, xr_hi, xi_hi, s_re, s_im;
+};
 template <int XT>
-__device__ __forceinline__ void build_table(const LutArgs& a, int j, int k, uint8_t* lds)
+__device__ __forceinline__ TableIn table_inputs(const LutArgs& a, int j, int k)
 {
     const int u = (k >> 3) & 3, i = k & 7;
     const int g = j / a.P, p = j - g * a.P;
     const int t_lo = (i < 4) ? 14 - 4 * i : 31 - 4 * i;
     const int c_lo = 64 * g + 16 * u + t_lo, c_hi = c_lo - 2;
-    const float s_re = a.scales[2 * p], s_im = a.scales[2 * p + 1];
+    const void* zero = &g_lut_zero;
+    const bool on_lo = c_lo < a.m, on_hi = c_hi < a.m;
+    TableIn t;
+    t.xr_lo = load_x<XT>(on_lo ? a.x_re : zero, on_lo ? c_lo : 0);
+    t.xi_lo = load_x<XT>(on_lo ? a.x_im : zero, on_lo ? c_lo : 0);
+    t.xr_hi = load_x<XT>(on_hi ? a.x_re : zero, on_hi ? c_hi : 0);
+    t.xi_hi = load_x<XT>(on_hi ? a.x_im : zero, on_hi ? c_hi : 0);
+    t.s_re = a.scales[2 * p];
+    t.s_im = a.scales[2 * p + 1];
+    return t;
+}
+
+// Table k from its inputs: the 16 sums of the pair's two codes.
+__device__ __forceinline__ void table_write(const LutArgs& a, int j, int k, const TableIn& t, uint8_t* lds)
+{
+    const int p = j % a.P;
     const float sg = (p < a.S) ? 1.0f : -1.0f;
-    float xr_lo = 0.0f, xi_lo = 0.0f, xr_hi = 0.0f, xi_hi = 0.0f;
-    if (c_lo < a.m) {
-        xr_lo = load_x<XT>(a.x_re, c_lo);
-        xi_lo = load_x<XT>(a.x_im, c_lo);
-    }
-    if (c_hi < a.m) {
-        xr_hi = load_x<XT>(a.x_re, c_hi);
-        xi_hi = load_x<XT>(a.x_im, c_hi);
-    }
     // contributions of codes 0 and 1 (codes 2, 3 are their negatives)
-    const float2 f_lo[2] = {make_float2(s_re * xr_lo, sg * (s_re * xi_lo)),
-                            make_float2(-sg * (s_im * xi_lo), s_im * xr_lo)};
-    const float2 f_hi[2] = {make_float2(s_re * xr_hi, sg * (s_re * xi_hi)),
-                            make_float2(-sg * (s_im * xi_hi), s_im * xr_hi)};
+    const float2 f_lo[2] = {make_float2(t.s_re * t.xr_lo, sg * (t.s_re * t.xi_lo)),
+                            make_float2(-sg * (t.s_im * t.xi_lo), t.s_im * t.xr_lo)};
+    const float2 f_hi[2] = {make_float2(t.s_re * t.xr_hi, sg * (t.s_re * t.xi_hi)),
+                            make_float2(-sg * (t.s_im * t.xi_hi), t.s_im * t.xr_hi)};
     float4* dst = reinterpret_cast<float4*>(lds + (size_t)k * kTableStride);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {  // entries 2q, 2q+1: c_hi = q >> 1, c_lo = 2(q & 1) + {0, 1}
@@ -109,11 +124,23 @@ __global__ __launch_bounds__(64 * W) void k_cgemv_lut(LutArgs a)
     const bool live = row < a.n;
     const uint4* src = a.units + row * a.UR + j0;
 
-    // the lane's units are in flight while the tables are built
+    // The first tables' inputs are loaded first, then the lane's units, so
+    // the tables are built (waiting for their inputs from L2) while the
+    // units come from HBM.  A thread without a first table loads table 0's
+    // inputs and writes nothing.
+    const int k0 = threadIdx.x;
+    const bool first = k0 < nj * kUnitTables;
+    const TableIn t0 = table_inputs<XT>(a, j0 + (first ? k0 : 0) / kUnitTables, first ? k0 : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4* zero = &g_lut_zero;
     uint4 w4[JB];
 #pragma unroll
-    for (int jj = 0; jj < JB; ++jj) w4[jj] = (live && jj < nj) ? src[jj] : make_uint4(0u, 0u, 0u, 0u);
-    for (int k = threadIdx.x; k < nj * kUnitTables; k += 64 * W) build_table<XT>(a, j0 + k / kUnitTables, k, lds);
+    for (int jj = 0; jj < JB; ++jj) w4[jj] = *((live && jj < nj) ? src + jj : zero);
+    if (first) table_write(a, j0 + k0 / kUnitTables, k0, t0, lds);
+    for (int k = k0 + 64 * W; k < nj * kUnitTables; k += 64 * W) {
+        const int j = j0 + k / kUnitTables;
+        table_write(a, j, k, table_inputs<XT>(a, j, k), lds);
+    }
     __syncthreads();
     if (!live) return;
 
