@@ -227,7 +227,7 @@ size_t fairy_cgemm_workspace_bytes(const fairy_clinear* L, int64_t M, int32_t xd
  * argument rules with batch replaced by M; acc is [P][4][M][n] for I8).
  * algo: AUTO, VALU (any dtype) or MFMA (BF16 or I8; codes expanded to
  * ternary {-1,0,1} planes feeding the matrix cores).  AUTO takes MFMA for
- * BF16 and I8 from M = 32.  The m limit of fairy_cgemv applies to the VALU
+ * BF16 and I8 from M = 16.  The m limit of fairy_cgemv applies to the VALU
  * path only: the matrix-core path streams the activations in chunks.
  * workspace: NULL (the call runs without a K split) or at least
  *   fairy_cgemm_workspace_bytes() bytes, 16-byte aligned, owned by the

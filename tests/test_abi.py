@@ -94,8 +94,8 @@ def test_cgemm_workspace_sizes():
     assert ws(256, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA) == 0          # 128 blocks
     assert ws(2048, F.FAIRY_BF16, F.FAIRY_ALGO_MFMA) == 0
     assert ws(16, F.FAIRY_BF16, F.FAIRY_ALGO_VALU) == 0
-    assert ws(16, F.FAIRY_BF16, F.FAIRY_ALGO_AUTO) == 0
-    assert ws(32, F.FAIRY_BF16, F.FAIRY_ALGO_AUTO) == 8 * 2 * 32 * 2048 * 4
+    assert ws(8, F.FAIRY_BF16, F.FAIRY_ALGO_AUTO) == 0
+    assert ws(16, F.FAIRY_BF16, F.FAIRY_ALGO_AUTO) == 8 * 2 * 16 * 2048 * 4
     assert ws(64, F.FAIRY_F32, F.FAIRY_ALGO_MFMA) == 0
     # plane counts that need several passes: none
     assert F.fairy_cgemm_workspace_bytes(F.make_clinear(2048, 2048, 3, 1, A, A), 16, F.FAIRY_BF16,
