@@ -60,14 +60,19 @@ __device__ __forceinline__ void unit_i8(const uint4 cw, int g, const uint8_t* xs
     }
 }
 
+// 4 rows (waves) per block: against 8, 2048^2 S=2 at B = 1 took 4.19 us
+// instead of 4.35-4.41 (same-box A/B); the bf16/fp32 kernel measured the
+// same either way and keeps 8
+constexpr int kThreadsLpI8 = 256;
+
 template <int P, int BCH>
-__global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp_i8(GemvArgs a)
+__global__ __launch_bounds__(kThreadsLpI8) void k_cgemv_lp_i8(GemvArgs a)
 {
     static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "power-of-two plane count");
     constexpr int GS = 64 / P;  // groups one step of the wave covers
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * (kThreadsLp / 64) + (threadIdx.x >> 6);
+    const int row = blockIdx.x * (kThreadsLpI8 / 64) + (threadIdx.x >> 6);
     const bool row_ok = row < a.n;
     const int p = lane % P, gl = lane / P;
     const int G = a.G;
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp_i8(GemvArgs a)
 #pragma unroll
     for (int u = 0; u < 2; ++u) cur[u] = *((row_ok && gl + u * GS < G) ? wl + 64 * u : zero);
     *dst0 = i8_reorder(x0);
-    for (int idx = threadIdx.x + kThreadsLp; idx < pieces; idx += kThreadsLp) {
+    for (int idx = threadIdx.x + kThreadsLpI8; idx < pieces; idx += kThreadsLpI8) {
         const uint4* src;
         uint4* dst;
         piece(idx, src, dst);
@@ -162,9 +167,9 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp_i8(GemvArgs a)
 template <int P, int BCH>
 hipError_t launch_lp_i8_t(const GemvArgs& a, hipStream_t s)
 {
-    const dim3 grid((a.n + (kThreadsLp / 64) - 1) / (kThreadsLp / 64), (a.B + BCH - 1) / BCH);
+    const dim3 grid((a.n + (kThreadsLpI8 / 64) - 1) / (kThreadsLpI8 / 64), (a.B + BCH - 1) / BCH);
     const size_t lds = (size_t)x_bytes_per_col(FAIRY_I8, a.m64) * BCH + 16;  // + the spare slot
-    hipLaunchKernelGGL((k_cgemv_lp_i8<P, BCH>), grid, dim3(kThreadsLp), lds, s, a);
+    hipLaunchKernelGGL((k_cgemv_lp_i8<P, BCH>), grid, dim3(kThreadsLpI8), lds, s, a);
     return hipGetLastError();
 }
 
