@@ -8,16 +8,19 @@ widely-linear complex form U, W (2048x2048 each), PhaseQuant-quantised with
 activations (batch 1 by default, N(0,1), seed 201).
 
 Each timed step reads a different copy of the packed weights from a pool of
->= 512 MiB, so the codes really stream from HBM (no L2 / Infinity-Cache
-reuse).  The K steps are captured once as a HIP graph and replayed, so the
-Python binding's launch cost is not measured; `value` is packed-weight GB/s
-over the timed steps.
+>= 512 MiB.  A timed run is exactly K steps captured as one HIP graph and
+replayed once untimed; 512 MiB are then read by another kernel, so that
+neither the L2 nor the 256 MB Infinity Cache holds any weight copy, and the
+next replay is timed with HIP events on the launch stream.  There are
+max(5, pool copies / K) such runs, over consecutive windows of the pool, and
+`ms_per_step` is their median; the Python binding's launch cost is not
+measured.  `value` is packed-weight GB/s at that time per step.
 
-Also reported: the roofline of the GEMV kernel (HBM-bound, algorithmic bytes
-per launch over the average launch time from HIP events on the launch
-stream), the CPU oracle on a bounded sample of the same workload, and the
-other rows of the path (conversion, PhaseQuant, pack, the MLP shapes, larger
-batches, the prefill GEMM on the matrix cores and on the VALUs).
+Also reported: the roofline of the GEMV kernel (HBM-bound: algorithmic bytes
+per launch over that time), the CPU oracle on a bounded sample of the same
+workload (all host cores and one core), and the other rows of the path
+(conversion, PhaseQuant, pack, the MLP shapes, larger batches, the prefill
+GEMM on the matrix cores and on the VALUs).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch B] [--sweep]
 """
@@ -43,6 +46,9 @@ GEMV_KERNEL = "k_cgemv_lp<bf16,P=4,BCH=1> (one row per wave, lane-fixed planes)"
 # WRITE_SIZE counters scaled by a plain copy's (profiles/gemv_lp_bf16_2048x2048_S2_B1.md);
 # None whenever the kernel has changed since those counters were taken
 GEMV_TRAFFIC_BYTES = 4380672
+# SQ_ACTIVE_INST_VALU x 4 cycles / (1024 SIMDs x kernel cycles) of GEMV_KERNEL
+# from the same profile; None whenever the kernel has changed since
+GEMV_VALU_BUSY = None
 POOL_BYTES = 512 << 20
 
 
@@ -95,6 +101,43 @@ class Bench:
         torch.cuda.synchronize()
         ms = self.ev_time(lambda i: g.replay(), 1) / steps
         return ms, g
+
+    def cold_runs(self, make_fn, steps, ncopy, flush):
+        """Timed runs of exactly `steps` launches each, every run on cold
+        weights.  Run r captures the launches make_fn(r*steps + j) (j <
+        steps; copy (r*steps + j) % ncopy) as a HIP graph, replays it once
+        untimed, reads `flush` (>= 512 MiB, read only) so that neither the
+        L2 nor the Infinity Cache holds any weight copy, then times one
+        replay with HIP events on the launch stream.  max(5, ncopy/steps)
+        runs, so the timed runs touch every copy of the pool.  Returns
+        (median ms per launch, [ms per launch of each run], distinct copies
+        read in the timed runs)."""
+        torch = self.torch
+        runs = max(5, math.ceil(ncopy / steps))
+        sink = torch.empty((flush.shape[0],), dtype=torch.float32, device="cuda")
+        per, touched = [], set()
+        for r in range(runs):
+            base = r * steps
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    for j in range(steps):
+                        make_fn(base + j)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.sum(flush, dim=1, out=sink)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            g.replay()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / steps)
+            touched.update((base + j) % ncopy for j in range(steps))
+            del g
+        return float(np.median(per)), per, len(touched)
 
     def widely_linear_layer(self, rows, cols, S, seed):
         """Real [rows][cols] N(0, 0.02^2) -> U, W -> S stages -> TILED64, all on the GPU."""
@@ -233,7 +276,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-rows", action="store_true", help="skip the other rows of the path")
     ap.add_argument("--sweep", action="store_true", help="also run the full-layer sweep (slow)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill", action="store_true",
                     help="only time the M=2048 prefill GEMM on the 2048x2048 S=2 layer (bf16 and int8, "
                          "matrix cores), e.g. under a profiler")
@@ -299,13 +342,16 @@ def main():
         F.fairy_cgemv(descs[i % ncopy], x_re, x_im, F.FAIRY_BF16, B, m, y_re, y_im, n)
 
     for i in range(args.warmup):
-        gemv(i)
+        gemv(ncopy - 1 - (i % ncopy))
     torch.cuda.synchronize()
     eager_y = (y_re.clone(), y_im.clone())
     eager_ms = bn.ev_time(gemv, min(args.steps, 200))
     y_re.zero_(); y_im.zero_()
+    # read-only cache flush: 512 MiB as [32768][4096] fp32 (row sums, the
+    # fastest streaming read among torch's reductions here)
+    flush = torch.ones((32768, 4096), dtype=torch.float32, device="cuda")
     t0 = time.perf_counter()
-    ms, graph = bn.graph_time(gemv, args.steps)
+    ms, run_ms, touched = bn.cold_runs(gemv, args.steps, ncopy, flush)
     wall = time.perf_counter() - t0
     if not (torch.equal(y_re, eager_y[0]) and torch.equal(y_im, eager_y[1])):
         raise SystemExit("graph replay output differs from the eager GEMV output")
@@ -316,22 +362,20 @@ def main():
     cdst.copy_(csrc)
     copy_ms = bn.ev_time(lambda i: cdst.copy_(csrc), 10)
     copy_gbs = 2 * csrc.numel() * 4 / (copy_ms * 1e-3) / 1e9
-    # and its streaming-read rate: row sums of 512 MiB as [32768][4096] fp32
-    # (512 MiB read, 128 KiB written; the fastest of the torch reductions
-    # tried here)
-    rsrc = torch.ones((32768, 4096), dtype=torch.float32, device="cuda")
-    rsum = torch.empty((32768,), dtype=torch.float32, device="cuda")
-    torch.sum(rsrc, dim=1, out=rsum)
-    read_ms = bn.ev_time(lambda i: torch.sum(rsrc, dim=1, out=rsum), 10)
-    read_gbs = rsrc.numel() * 4 / (read_ms * 1e-3) / 1e9
-    del csrc, cdst, rsrc, rsum
+    # and its streaming-read rate: the flush read itself (512 MiB read, 128 KiB written)
+    rsum = torch.empty((flush.shape[0],), dtype=torch.float32, device="cuda")
+    torch.sum(flush, dim=1, out=rsum)
+    read_ms = bn.ev_time(lambda i: torch.sum(flush, dim=1, out=rsum), 10)
+    read_gbs = flush.numel() * 4 / (read_ms * 1e-3) / 1e9
+    del csrc, cdst, rsum, flush
     alg_bytes = packed_bytes + B * m * 2 * 2 + B * n * 2 * 4
     hbm_achieved = alg_bytes / (ms * 1e-3) / 1e9
     # the multiplication-free form: two fp32 adds per code per batch column
     alg_adds = 2 * P * n * m * B
     alu_achieved = alg_adds / (ms * 1e-3) / 1e12
-    log(f"GEMV B={B}: graph {ms * 1e3:.2f} us/launch ({gbs:.0f} GB/s packed), eager {eager_ms * 1e3:.2f} us/call, "
-        f"capture+replay wall {wall:.3f}s for {args.steps}")
+    log(f"GEMV B={B}: cold graph runs {ms * 1e3:.2f} us/launch median of {len(run_ms)} "
+        f"({', '.join(f'{r * 1e3:.2f}' for r in run_ms)}), {gbs:.0f} GB/s packed; eager {eager_ms * 1e3:.2f} "
+        f"us/call; {touched} distinct copies in the timed runs; wall {wall:.3f}s")
 
     result = {
         "metric": "GB/s & % HBM peak, 2-bit complex GEMV at LLaMA-2-7B shapes; prefill TOPS",
@@ -352,27 +396,34 @@ def main():
                         f"packed TILED64, bf16 activations, batch {B}",
             "n": n, "m": m, "stages": S, "planes": P, "batch": B,
             "packed_bytes": packed_bytes, "weight_pool_bytes": packed_bytes * ncopy,
+            "weight_bytes_timed_per_run": packed_bytes * min(args.steps, ncopy),
             "complex_weights_per_s": P * n * m / (ms * 1e-3),
             "hbm_frac_packed": round(gbs / HBM_PEAK_GBS, 4),
         },
-        # Decoding costs ~3.5 VALU instructions per code (4 v_dot2 + 3 bit
-        # operations per code pair), so the kernel is bound by the vector ALU,
-        # not by HBM: counters put the VALU busy and HBM far below it.
+        # The kernel streams the packed codes once (counter-measured traffic
+        # within a few % of the algorithmic bytes), so its roof is HBM; the
+        # vector ALU busy fraction from the counters stands beside it.
         "roofline": {
-            "bound": "alu",
-            "achieved": round(alu_achieved, 3),
-            "peak": round(VALU_PEAK_TOPS, 2),
-            "unit": "Tops/s (algorithmic fp32 adds)",
-            "frac": round(alu_achieved / VALU_PEAK_TOPS, 4),
+            "bound": "hbm",
+            "achieved": round(hbm_achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(hbm_achieved / HBM_PEAK_GBS, 4),
             "traffic": GEMV_TRAFFIC_BYTES if B == 1 else None,
             "kernel": GEMV_KERNEL,
-            "alg_adds_per_launch": alg_adds,
-            "hbm": {"achieved": round(hbm_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(hbm_achieved / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": alg_bytes,
-                    "measured_copy_GBps": round(copy_gbs, 1),
-                    "frac_of_measured_copy": round(hbm_achieved / copy_gbs, 4),
-                    "measured_read_GBps": round(read_gbs, 1),
-                    "frac_of_measured_read": round(hbm_achieved / read_gbs, 4)},
+            "alg_bytes_per_launch": alg_bytes,
+            "kernel_us_per_launch": round(ms * 1e3, 4),
+            "timing": f"median of {len(run_ms)} cold runs of {args.steps} graph-replayed launches each "
+                      f"(HIP events on the launch stream; 512 MiB read between runs)",
+            "run_us_per_launch": [round(r * 1e3, 4) for r in run_ms],
+            "distinct_weight_copies_timed": touched,
+            "measured_copy_GBps": round(copy_gbs, 1),
+            "frac_of_measured_copy": round(hbm_achieved / copy_gbs, 4),
+            "measured_read_GBps": round(read_gbs, 1),
+            "frac_of_measured_read": round(hbm_achieved / read_gbs, 4),
+            "valu": {"alg_adds_per_launch": alg_adds, "alg_Tadds_per_s": round(alu_achieved, 3),
+                     "peak_Tlane_ops_per_s": round(VALU_PEAK_TOPS, 2),
+                     "busy_frac_counters": GEMV_VALU_BUSY if B == 1 else None},
             "eager_ms_per_call": eager_ms,
         },
     }
@@ -430,6 +481,10 @@ def main():
                 msg = bn.gemm_rate(L2, d1, 2048, F.FAIRY_I8, F.FAIRY_ALGO_MFMA)
                 rows_out["gemm_5504x2048_M2048_i8_mfma"] = gemm_entry(msg, 4, L2["n"], L2["m"], 2048,
                                                                       MFMA_PEAK_TFLOPS["i8"])
+                # the same prefill on the vector ALUs (direct decode, no matrix cores)
+                for dt, dn in ((F.FAIRY_BF16, "bf16"), (F.FAIRY_I8, "i8")):
+                    msg = bn.gemm_rate(L2, d1, 2048, dt, F.FAIRY_ALGO_VALU, iters=2)
+                    rows_out[f"gemm_5504x2048_M2048_{dn}_valu"] = gemm_entry(msg, 4, L2["n"], L2["m"], 2048)
             del L2
             torch.cuda.empty_cache()
         d0 = F.make_clinear(n, m, S, 1, L["packed"], L["scales"])
@@ -461,25 +516,46 @@ def main():
     # ---- CPU oracle baseline (bounded sample of the same workload) ---------------------
     if not args.no_cpu:
         import oracle
-        cores = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1))
         Rh = synth.real_layer(4096, 4096, 200)
         ur, ui, wr, wi = oracle.real_to_complex(Rh, n, m, f32=True)
         cu, su, _, _ = oracle.phasequant(ur, ui, S, want_resid=False)
         cw, sw, _, _ = oracle.phasequant(wr, wi, S, want_resid=False)
         oc = np.concatenate([cu, cw]); osc = np.concatenate([su, sw])
         xr, xi = synth.bf16_to_f32(rb), synth.bf16_to_f32(ib)
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            oracle.cgemv_dense(oc, osc, S, True, xr, xi)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds or reps >= 100000:
-                break
+
+        def oracle_rate(threads, seconds):
+            used = oracle.set_threads(threads)
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                oracle.cgemv_dense(oc, osc, S, True, xr, xi)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds or reps >= 100000:
+                    return used, reps, el
+
+        # all the host cores this process may use (the box gives one GPU's
+        # share of the host; OMP_NUM_THREADS states it), then one core
+        all_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        cores, reps, el = oracle_rate(all_threads, args.cpu_seconds)
+        _, reps1, el1 = oracle_rate(1, args.cpu_seconds / 2)
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        cpu_model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         result["cpu_baseline"] = {
             "value": round(packed_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{reps} full GEMVs of the same 2048x2048 S=2 widely-linear layer, batch {B}, "
-                      f"dense fp64 oracle, {el:.1f}s",
+                      f"dense fp64 oracle over output rows on {cores} threads, {el:.1f}s",
+            "single_thread": {"value": round(packed_bytes * reps1 / el1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"{reps1} GEMVs on 1 thread, {el1:.1f}s"},
+            "cpu_model": cpu_model, "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
         }
 
     print(json.dumps(result), flush=True)

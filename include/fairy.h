@@ -13,8 +13,11 @@
  *   [Fairy2i article]  "复数域低比特量化框架Fairy2i" (hotelren.com/news/3072820):
  *                      §2.1 widely-linear conversion, §3.1 codebook and phase
  *                      rule, §3.2 axis scales, §4.1 recursive residual,
- *                      §4.2 multiplication-free matmul, §5.3 "verify split
- *                      real/imag handling".
+ *                      §4.2 multiplication-free matmul, §5.2 (troubleshooting)
+ *                      item 3: check that real and imaginary parts are kept
+ *                      and handled apart.
+ *   [iFairy press article] bestcxt.com article on iFairy, §一: two bits per
+ *                      weight, one eighth of the storage of fp16.
  *   [iFairy talk]      minutes of the talk "iFairy: 2-bit复数基座大模型"
  *                      (news.43b.com.cn/a/865699.html), §2.3.1: times i is a
  *                      real/imag swap with a negation.
@@ -38,7 +41,7 @@
  *    returns an error launches nothing and writes nothing.  Calls never
  *    throw, abort or print.
  *  - Complex data is always split into separate real and imaginary planes
- *    (structure of arrays), as [Fairy2i article §5.3] asks.
+ *    (structure of arrays), as [Fairy2i article §5.2, item 3] asks.
  *  - Inputs must be finite.  NaN/Inf inputs are undefined behaviour (not
  *    checked).
  */
@@ -154,7 +157,13 @@ fairy_status fairy_phasequant(const float* w_re, const float* w_im, int64_t coun
                               uint8_t* codes, float* scales, float* resid_re, float* resid_im,
                               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Number of uint32 words of a packed buffer; -1 for invalid arguments. */
+/* ---- Packed storage ------------------------------------------------------------
+ * [iFairy press article §一: a weight takes two bits, so a model takes one
+ * eighth of its fp16 storage; Fairy2i article §5.2 item 3: the device must
+ * support the complex storage format, real and imaginary parts kept apart]
+ * The pages fix no word layout: ROW16 and TILED64 above are this library's.
+ *
+ * Number of uint32 words of a packed buffer; -1 for invalid arguments. */
 int64_t fairy_packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout);
 
 /* Pack codes [planes][rows][m] (uint8, values 0..3; higher bits ignored)
@@ -340,8 +349,10 @@ fairy_status fairy_layer_load(const void* buf, size_t bytes, uint32_t* packed, f
  *   causal           : 0 or 1; causal needs sk >= sq (INVALID_ARG otherwise)
  * One fused pass on the matrix cores (online softmax, nothing of size
  * sq x sk in memory).  Scores are exact fp32 sums of the bf16 products;
- * the weights are carried to ~2^-17 relative precision, so o is within
- * 2e-5 relative L2 of the exact result on the same bf16 inputs. */
+ * the weights are carried to ~2^-17 relative precision (each weight's
+ * error is at most 2^-17 of it, so o is off by at most 2^-17 of the
+ * weighted sum of |v|), and o is within 1e-5 relative L2 of the exact
+ * result on the same bf16 inputs for values that do not cancel. */
 fairy_status fairy_cattention(const void* q_re, const void* q_im, const void* k_re, const void* k_im,
                               const void* v_re, const void* v_im, int32_t dtype, int32_t heads,
                               int64_t sq, int64_t sk, int32_t d, float scale, int32_t causal,

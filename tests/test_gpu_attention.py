@@ -1,6 +1,8 @@
 """GPU parity of the fused complex attention against the fp64 oracle on the
-same bf16 inputs: relative L2 error <= 2e-5 (the bound fairy.h states: exact
-scores, weights carried as bf16 hi + lo pairs, fp32 accumulation)."""
+same bf16 inputs: relative L2 error <= 1e-5, the float bound of the layer
+itself (fairy.h: exact scores, weights carried as bf16 hi + lo pairs to
+~2^-17 relative precision, fp32 accumulation; measured errors 1.3e-6 to
+2.3e-6)."""
 import numpy as np
 import pytest
 
@@ -10,7 +12,7 @@ from bit_complex_weight_amd import synth
 from tests._gpu import dev, host, log, rel_l2, torch
 
 pytestmark = pytest.mark.gpu
-TOL = 2e-5
+TOL = 1e-5
 
 
 def make(h, sq, sk, d, seed):

@@ -359,9 +359,8 @@ def test_gemm_mfma_deterministic():
 @pytest.mark.parametrize("algo", [F.FAIRY_ALGO_MFMA, F.FAIRY_ALGO_VALU])
 def test_prefill_gemm_sampled(n, xdtype, algo):
     """The prefill case at full size: M = 2048 tokens, 2048-column complex
-    layers with 2048 or 5504 rows, S = 2 widely-linear; sampled outputs."""
-    if algo == F.FAIRY_ALGO_VALU and n == 5504:
-        pytest.skip("VALU prefill at 5504 rows is covered at 2048 rows (same kernel, slow)")
+    layers with 2048 or 5504 rows, S = 2 widely-linear; sampled outputs
+    (every algorithm: the vector-ALU path against the matrix-core path)."""
     log(f"prefill M=2048 n={n} m=2048 S=2 dt={xdtype} algo={algo}")
     S, m, M = 2, 2048, 2048
     codes = synth.random_codes((2 * S, n, m), 400 + n)
@@ -384,3 +383,35 @@ def test_prefill_gemm_sampled(n, xdtype, algo):
     if xdtype == F.FAIRY_I8:
         want_acc = oracle.cgemv_acc_i64(codes[:, rows], xr[toks], xi[toks])
         assert np.array_equal(acc[:, :, toks][:, :, :, rows].astype(np.int64), want_acc)
+
+
+@pytest.mark.parametrize("xdtype", [F.FAIRY_BF16, F.FAIRY_I8])
+def test_prefill_gemm_full_output(xdtype):
+    """The prefill case at full size compared on every output: M = 2048
+    tokens through the 2048x2048 S = 2 widely-linear layer, on the matrix
+    cores and on the vector ALUs.  int8: every raw accumulator exact; floats
+    within the bound.  The oracle runs on all host cores (each output is
+    still one ordered sum)."""
+    S, n, m, M = 2, 2048, 2048, 2048
+    log(f"prefill full output M={M} n={n} m={m} S={S} dt={xdtype}")
+    codes = synth.random_codes((2 * S, n, m), 410)
+    scales = synth.random_scales(2 * S, 411)
+    layer = layer_from_codes(codes, scales, S, True)
+    oracle.set_threads(0)
+    if xdtype == F.FAIRY_BF16:
+        rb, ib = synth.bf16_gaussian((M, m), 412)
+        xr, xi = synth.bf16_to_f32(rb), synth.bf16_to_f32(ib)
+        args = (dev(rb), dev(ib))
+    else:
+        xr, xi = synth.int8_uniform((M, m), 413)
+        args = (dev(xr), dev(xi))
+    wr, wi = oracle.cgemv_dense(codes, scales, S, True, xr.astype(np.float64), xi.astype(np.float64))
+    want_acc = oracle.cgemv_acc_i64(codes, xr, xi) if xdtype == F.FAIRY_I8 else None
+    for algo in (F.FAIRY_ALGO_MFMA, F.FAIRY_ALGO_VALU):
+        yr, yi, acc = run_gemv(layer, *args, xdtype, M, want_acc=xdtype == F.FAIRY_I8, gemm=True, algo=algo)
+        err = rel_l2(yr + 1j * yi, wr + 1j * wi)
+        log(f"  algo={algo} rel_l2={err:.3e}")
+        assert err <= TOL
+        if want_acc is not None:
+            assert np.array_equal(acc.astype(np.int64), want_acc)
+        del acc

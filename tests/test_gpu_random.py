@@ -2,8 +2,8 @@
 drawn from the argument space (plane counts, ragged rows, columns and
 tokens, every activation type and algorithm, with and without the GEMM
 workspace), each compared with the fp64 / exact oracle to the same bounds
-as the fixed cases: <= 1e-5 relative L2 for float outputs (2e-5 for
-attention), int32 accumulators exact."""
+as the fixed cases: <= 1e-5 relative L2 for float outputs (attention
+included), int32 accumulators exact."""
 import numpy as np
 import pytest
 
@@ -119,4 +119,4 @@ def test_random_attention(i):
     w_re, w_im = oracle.cattention(*vals, scale, bool(causal))
     err = rel_l2(host(o_re) + 1j * host(o_im), w_re + 1j * w_im)
     log(f"  rel_l2={err:.3e}")
-    assert err <= 2e-5
+    assert err <= TOL
