@@ -8,10 +8,13 @@ widely-linear complex form U, W (2048x2048 each), PhaseQuant-quantised with
 activations (batch 1 by default, N(0,1), seed 201).
 
 Each timed step reads a different copy of the packed weights from a pool of
->= 512 MiB.  A timed run is exactly K steps captured as one HIP graph and
+>= 512 MiB.  A timed run is exactly K steps captured as one HIP graph
+between two event record nodes (the graph's first and last node) and
 replayed once untimed; 512 MiB are then read by another kernel, so that
 neither the L2 nor the 256 MB Infinity Cache holds any weight copy, and the
-next replay is timed with HIP events on the launch stream.  There are
+time between the two event nodes of the next replay is the run's time (HIP
+events around a whole replay add a fixed ~10 us per graph launch, reported
+beside it).  There are
 max(5, pool copies / K) such runs, over consecutive windows of the pool, and
 `ms_per_step` is their median; the Python binding's launch cost is not
 measured.  `value` is packed-weight GB/s at that time per step.
@@ -102,42 +105,114 @@ class Bench:
         ms = self.ev_time(lambda i: g.replay(), 1) / steps
         return ms, g
 
+    def hip(self):
+        """HIP runtime entry points for graphs with timestamp nodes, taken from
+        the runtime torch itself loaded (the process keeps one HIP runtime)."""
+        if getattr(self, "_hip", None) is None:
+            import ctypes
+            h = ctypes.CDLL(os.path.join(os.path.dirname(self.torch.__file__), "lib", "libamdhip64.so"))
+            h.hipGetErrorString.restype = ctypes.c_char_p
+            self._hip = (h, ctypes)
+        return self._hip
+
+    def timed_graph(self, fn, steps, stream):
+        """Capture fn(j), j < steps, on `stream` into a HIP graph with an event
+        record node before its first node and one after its last, so the
+        time between the two events is exactly the captured launches (HIP
+        events around a whole graph launch also count a fixed ~10 us that
+        every graph launch costs, whatever its kernels).  Returns
+        (graph exec, event before, event after, cleanup)."""
+        torch = self.torch
+        h, c = self.hip()
+        P = c.c_void_p
+
+        def ck(rc, what):
+            if rc != 0:
+                raise SystemExit(f"{what} failed: {h.hipGetErrorString(rc).decode()}")
+
+        sp = P(stream.cuda_stream)
+        e0, e1 = P(), P()
+        ck(h.hipEventCreate(c.byref(e0)), "hipEventCreate")
+        ck(h.hipEventCreate(c.byref(e1)), "hipEventCreate")
+        ck(h.hipStreamBeginCapture(sp, 0), "hipStreamBeginCapture")
+        with torch.cuda.stream(stream):
+            for j in range(steps):
+                fn(j)
+        g = P()
+        ck(h.hipStreamEndCapture(sp, c.byref(g)), "hipStreamEndCapture")
+        n = c.c_size_t(0)
+        ck(h.hipGraphGetNodes(g, None, c.byref(n)), "hipGraphGetNodes")
+        nodes = (P * n.value)()
+        ck(h.hipGraphGetNodes(g, nodes, c.byref(n)), "hipGraphGetNodes")
+        nr = c.c_size_t(0)
+        ck(h.hipGraphGetRootNodes(g, None, c.byref(nr)), "hipGraphGetRootNodes")
+        roots = (P * nr.value)()
+        ck(h.hipGraphGetRootNodes(g, roots, c.byref(nr)), "hipGraphGetRootNodes")
+        leaves = []
+        for i in range(n.value):
+            nd = c.c_size_t(0)
+            ck(h.hipGraphNodeGetDependentNodes(P(nodes[i]), None, c.byref(nd)), "hipGraphNodeGetDependentNodes")
+            if nd.value == 0:
+                leaves.append(nodes[i])
+        n0, n1 = P(), P()
+        ck(h.hipGraphAddEventRecordNode(c.byref(n0), g, None, c.c_size_t(0), e0), "hipGraphAddEventRecordNode")
+        for r in roots:
+            ck(h.hipGraphAddDependencies(g, c.byref(n0), c.byref(P(r)), c.c_size_t(1)), "hipGraphAddDependencies")
+        la = (P * len(leaves))(*leaves)
+        ck(h.hipGraphAddEventRecordNode(c.byref(n1), g, la, c.c_size_t(len(leaves)), e1), "hipGraphAddEventRecordNode")
+        ge = P()
+        ck(h.hipGraphInstantiate(c.byref(ge), g, None, None, c.c_size_t(0)), "hipGraphInstantiate")
+
+        def launch():
+            ck(h.hipGraphLaunch(ge, sp), "hipGraphLaunch")
+
+        def elapsed_ms():
+            ms = c.c_float()
+            ck(h.hipEventElapsedTime(c.byref(ms), e0, e1), "hipEventElapsedTime")
+            return ms.value
+
+        def cleanup():
+            h.hipGraphExecDestroy(ge)
+            h.hipGraphDestroy(g)
+            h.hipEventDestroy(e0)
+            h.hipEventDestroy(e1)
+
+        return launch, elapsed_ms, cleanup
+
     def cold_runs(self, make_fn, steps, ncopy, flush):
         """Timed runs of exactly `steps` launches each, every run on cold
         weights.  Run r captures the launches make_fn(r*steps + j) (j <
-        steps; copy (r*steps + j) % ncopy) as a HIP graph, replays it once
-        untimed, reads `flush` (>= 512 MiB, read only) so that neither the
-        L2 nor the Infinity Cache holds any weight copy, then times one
-        replay with HIP events on the launch stream.  max(5, ncopy/steps)
-        runs, so the timed runs touch every copy of the pool.  Returns
-        (median ms per launch, [ms per launch of each run], distinct copies
-        read in the timed runs)."""
+        steps; copy (r*steps + j) % ncopy) as a HIP graph between two event
+        record nodes, replays it once untimed, reads `flush` (>= 512 MiB,
+        read only) so that neither the L2 nor the Infinity Cache holds any
+        weight copy, then replays it again: the time between its two event
+        nodes is the run's time.  max(5, ncopy/steps) runs, so the timed runs
+        touch every copy of the pool.  Returns (median ms per launch, [ms per
+        launch of each run], distinct copies read in the timed runs, median
+        ms per launch timed around the whole graph launch)."""
         torch = self.torch
         runs = max(5, math.ceil(ncopy / steps))
         sink = torch.empty((flush.shape[0],), dtype=torch.float32, device="cuda")
-        per, touched = [], set()
+        st = torch.cuda.Stream()
+        per, outer, touched = [], [], set()
         for r in range(runs):
             base = r * steps
-            g = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(g, stream=cap):
-                    for j in range(steps):
-                        make_fn(base + j)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.sum(flush, dim=1, out=sink)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(self.stream)
-            g.replay()
-            e1.record(self.stream)
-            torch.cuda.synchronize()
-            per.append(e0.elapsed_time(e1) / steps)
+            launch, elapsed_ms, cleanup = self.timed_graph(lambda j: make_fn(base + j), steps, st)
+            launch()
+            with torch.cuda.stream(st):
+                torch.sum(flush, dim=1, out=sink)
+            o0 = torch.cuda.Event(enable_timing=True)
+            o1 = torch.cuda.Event(enable_timing=True)
+            o0.record(st)
+            launch()
+            o1.record(st)
+            st.synchronize()
+            per.append(elapsed_ms() / steps)
+            outer.append(o0.elapsed_time(o1) / steps)
             touched.update((base + j) % ncopy for j in range(steps))
-            del g
-        return float(np.median(per)), per, len(touched)
+            cleanup()
+        torch.cuda.synchronize()
+        return float(np.median(per)), per, len(touched), float(np.median(outer))
 
     def widely_linear_layer(self, rows, cols, S, seed):
         """Real [rows][cols] N(0, 0.02^2) -> U, W -> S stages -> TILED64, all on the GPU."""
@@ -351,7 +426,7 @@ def main():
     # fastest streaming read among torch's reductions here)
     flush = torch.ones((32768, 4096), dtype=torch.float32, device="cuda")
     t0 = time.perf_counter()
-    ms, run_ms, touched = bn.cold_runs(gemv, args.steps, ncopy, flush)
+    ms, run_ms, touched, ms_outer = bn.cold_runs(gemv, args.steps, ncopy, flush)
     wall = time.perf_counter() - t0
     if not (torch.equal(y_re, eager_y[0]) and torch.equal(y_im, eager_y[1])):
         raise SystemExit("graph replay output differs from the eager GEMV output")
@@ -413,8 +488,10 @@ def main():
             "kernel": GEMV_KERNEL,
             "alg_bytes_per_launch": alg_bytes,
             "kernel_us_per_launch": round(ms * 1e3, 4),
-            "timing": f"median of {len(run_ms)} cold runs of {args.steps} graph-replayed launches each "
-                      f"(HIP events on the launch stream; 512 MiB read between runs)",
+            "timing": f"median of {len(run_ms)} cold runs of {args.steps} graph-replayed launches each, "
+                      f"between two event record nodes of the graph (the first and last node); 512 MiB "
+                      f"read before each timed replay",
+            "us_per_launch_incl_graph_launch": round(ms_outer * 1e3, 4),
             "run_us_per_launch": [round(r * 1e3, 4) for r in run_ms],
             "distinct_weight_copies_timed": touched,
             "measured_copy_GBps": round(copy_gbs, 1),

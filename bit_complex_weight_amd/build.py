@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfairy.so")
 SOURCES = ["fairy_api.hip", "fairy_quant.hip", "fairy_gemv.hip", "fairy_gemv_bf16.hip",
-           "fairy_gemv_f32.hip", "fairy_gemv_i8.hip", "fairy_gemm.hip", "fairy_gemm_mfma.hip",
+           "fairy_gemv_f32.hip", "fairy_gemv_i8.hip", "fairy_gemm.hip", "fairy_gemm_mfma.hip", "fairy_gemm_valu.hip",
            "fairy_layer.hip", "fairy_attention.hip", "fairy_gemv_lut.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

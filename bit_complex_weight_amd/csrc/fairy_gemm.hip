@@ -6,6 +6,9 @@
 
 namespace fairy {
 
+// token count from which the VALU path maps lanes to tokens
+constexpr int64_t kValuTokensMin = 64;
+
 // AUTO: the matrix cores from 16 tokens (measured without a workspace: at
 // M = 16 they beat the VALU kernels on the 2048x2048, 5504x2048 and
 // 2048x5504 S=2 layers, at M = 8 they lose on two of the three)
@@ -32,8 +35,14 @@ hipError_t launch_cgemm(const LayerArgs& L, const void* x_re, const void* x_im, 
         const gemv::GemvArgs a = gemv::make_args(L, x_re, x_im, M, ldx, y_re, y_im, ldy, acc);
         return launch_cgemm_mfma(a, xdtype, workspace, s);
     }
-    // VALU path: the decode kernel streams the token rows through LDS in
-    // chunks, re-reading the (L2-resident) codes per chunk.
+    // VALU path.  From a wave's worth of tokens: lanes are tokens, the code
+    // words are decoded once per wave on the scalar unit.  Otherwise (and
+    // for fp32 activations) the decode kernel streams the token rows
+    // through LDS in chunks, re-reading the (L2-resident) codes per chunk.
+    if (M >= kValuTokensMin && cgemm_valu_tokens_supported(xdtype, L.m, L.planes)) {
+        const gemv::GemvArgs a = gemv::make_args(L, x_re, x_im, M, ldx, y_re, y_im, ldy, acc);
+        return launch_cgemm_valu(a, xdtype, s);
+    }
     return launch_cgemv(L, x_re, x_im, xdtype, M, ldx, y_re, y_im, ldy, acc, s);
 }
 

@@ -631,6 +631,12 @@ GemvArgs make_args(const LayerArgs& L, const void* x_re, const void* x_im, int64
 
 }  // namespace gemv
 
+// vector-ALU prefill with lanes as tokens (fairy_gemm_valu.hip); a.B is the
+// token count.  Supported for bf16 and int8 (m <= 65536) activations and
+// P in {1, 2, 3, 4, 6, 8, 16}.
+bool cgemm_valu_tokens_supported(int32_t xdtype, int64_t m, int32_t planes);
+hipError_t launch_cgemm_valu(const gemv::GemvArgs& a, int32_t xdtype, hipStream_t s);
+
 // matrix-core prefill (fairy_gemm_mfma.hip); a.B is the token count.
 // workspace (nullable): fp32 partial sums for the split-K launch, of
 // cgemm_mfma_workspace_bytes() bytes (0: no split for this shape).
