@@ -257,6 +257,90 @@ class Bench:
         ms, _ = self.graph_time(f, steps)
         return ms
 
+    def layer_step_rate(self, layers, B, grouped, steps=50, seed=206):
+        """One step = the seven projections of a layer on one batch of bf16
+        activations (the attention input for q, k, v and o; the MLP input for
+        gate, up and down: widths 2048 / 2048 / 5504), either as seven
+        fairy_cgemv launches or as four (q+k+v and gate+up grouped with
+        fairy_cgemv_group).  Every projection reads its own pool of weight
+        copies; timed between the event nodes of a graph of `steps` steps.
+        Returns ms per step."""
+        torch, F = self.torch, self.F
+        pools = {k: self.pool(L) for k, L in layers.items()}
+        xs, ys = {}, {}
+        for k, L in layers.items():
+            m = L["m"]
+            if m not in xs:
+                xr, xi = self.synth.bf16_gaussian((B, m), seed + m)
+                xs[m] = (self.dev(xr), self.dev(xi))
+            ys[k] = (torch.empty((B, L["n"]), dtype=torch.float32, device="cuda"),
+                     torch.empty((B, L["n"]), dtype=torch.float32, device="cuda"))
+
+        def one(k, i):
+            L = layers[k]
+            descs = pools[k][1]
+            xr, xi = xs[L["m"]]
+            F.fairy_cgemv(descs[i % len(descs)], xr, xi, F.FAIRY_BF16, B, L["m"], ys[k][0], ys[k][1], L["n"])
+
+        def group(ks, i):
+            L0 = layers[ks[0]]
+            xr, xi = xs[L0["m"]]
+            F.fairy_cgemv_group([pools[k][1][i % len(pools[k][1])] for k in ks], xr, xi, F.FAIRY_BF16, B, L0["m"],
+                                [ys[k][0] for k in ks], [ys[k][1] for k in ks], [layers[k]["n"] for k in ks])
+
+        def step(i):
+            if grouped:
+                group(["q", "k", "v"], i)
+                one("o", i)
+                group(["gate", "up"], i)
+                one("down", i)
+            else:
+                for k in ("q", "k", "v", "o", "gate", "up", "down"):
+                    one(k, i)
+
+        step(0)
+        st = torch.cuda.Stream()
+        launch, elapsed_ms, cleanup = self.timed_graph(step, steps, st)
+        launch()
+        launch()
+        st.synchronize()
+        ms = elapsed_ms() / steps
+        cleanup()
+        del pools
+        torch.cuda.empty_cache()
+        return ms
+
+    def group_rate(self, Ls, B, steps=100, seed=207):
+        """fairy_cgemv_group over layers Ls (each with its own pool of
+        copies) against the same layers launched one by one; ms per step."""
+        torch, F = self.torch, self.F
+        pools = [self.pool(L) for L in Ls]
+        m = Ls[0]["m"]
+        xr, xi = self.synth.bf16_gaussian((B, m), seed)
+        xr, xi = self.dev(xr), self.dev(xi)
+        ys = [(torch.empty((B, L["n"]), dtype=torch.float32, device="cuda"),
+               torch.empty((B, L["n"]), dtype=torch.float32, device="cuda")) for L in Ls]
+        out = {}
+        for grouped in (True, False):
+            def step(i):
+                if grouped:
+                    F.fairy_cgemv_group([p[1][i % len(p[1])] for p in pools], xr, xi, F.FAIRY_BF16, B, m,
+                                        [y[0] for y in ys], [y[1] for y in ys], [L["n"] for L in Ls])
+                else:
+                    for L, p, y in zip(Ls, pools, ys):
+                        F.fairy_cgemv(p[1][i % len(p[1])], xr, xi, F.FAIRY_BF16, B, m, y[0], y[1], L["n"])
+            step(0)
+            st = torch.cuda.Stream()
+            launch, elapsed_ms, cleanup = self.timed_graph(step, steps, st)
+            launch()
+            launch()
+            st.synchronize()
+            out["grouped" if grouped else "separate"] = elapsed_ms() / steps
+            cleanup()
+        del pools
+        torch.cuda.empty_cache()
+        return out
+
     def lut_rate(self, L, descs, steps=200, seed=202):
         """Table-lookup GEMV, batch 1, bf16 activations, over the weight pool."""
         torch, F = self.torch, self.F
@@ -361,6 +445,9 @@ def main():
     ap.add_argument("--lut", action="store_true",
                     help="only time the table-lookup GEMV beside the direct one, batch 1, on the 2048x2048 "
                          "S=2 layer, e.g. under a profiler")
+    ap.add_argument("--layer", action="store_true",
+                    help="only time the whole S=2 layer step (7 projections, batch 1 and 4) as 7 launches and as "
+                         "4 with the grouped GEMV, e.g. under a profiler")
     ap.add_argument("--calib", action="store_true",
                     help="only measure the ceilings: a plain 256 MiB copy (the byte-counter calibration "
                          "kernel), 4 MiB and 32 MiB copy launches and tiny launches in HIP graphs")
@@ -388,6 +475,19 @@ def main():
         ms_l = bn.lut_rate(L, descs, steps=args.steps)
         ms_d = bn.gemv_rate(L, descs, 1, F.FAIRY_BF16, steps=args.steps)
         print(json.dumps({"gemv_lut_2048x2048_bf16_B1": lut_entry(ms_l, ms_d, L)}), flush=True)
+        return
+    if args.layer:
+        proj = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
+                "gate": (11008, 4096), "up": (11008, 4096), "down": (4096, 11008)}
+        layers = {name: bn.widely_linear_layer(rr, cc, 2, 520 + i) for i, (name, (rr, cc)) in enumerate(proj.items())}
+        tot = sum(L["packed_bytes"] for L in layers.values())
+        out = {}
+        for B in (1, 4):
+            for grouped in (False, True):
+                ms_l = bn.layer_step_rate(layers, B, grouped, steps=args.steps)
+                out[f"layer_step_S2_B{B}_{'grouped' if grouped else 'separate'}"] = {
+                    "ms": ms_l, "packed_GB/s": tot / (ms_l * 1e-3) / 1e9}
+        print(json.dumps(out), flush=True)
         return
     if args.prefill:
         L = bn.widely_linear_layer(4096, 4096, 2, seed=200)
@@ -536,12 +636,24 @@ def main():
         ms1 = ms if B == 1 else bn.gemv_rate(L, descs, 1, F.FAIRY_BF16, steps=200)
         rows_out["gemv_lut_2048x2048_bf16_B1"] = lut_entry(bn.lut_rate(L, descs), ms1, L)
         del copies, descs
+        # q, k, v in one launch (three pools of the same quantised layer)
+        gq = bn.group_rate([L, L, L], 1)
+        rows_out["gemv_group_qkv_3x2048x2048_bf16_B1"] = {
+            "ms": gq["grouped"], "separate_ms": gq["separate"],
+            "packed_GB/s": 3 * packed_bytes / (gq["grouped"] * 1e-3) / 1e9,
+            "separate_packed_GB/s": 3 * packed_bytes / (gq["separate"] * 1e-3) / 1e9}
         torch.cuda.empty_cache()
         # MLP shapes (gate/up: 11008x4096, down: 4096x11008)
         for name, (rr, cc, sd) in {"gate_up_5504x2048": (11008, 4096, 300),
                                    "down_2048x5504": (4096, 11008, 302)}.items():
             L2 = bn.widely_linear_layer(rr, cc, 2, sd)
             c2, d2 = bn.pool(L2)
+            if name.startswith("gate"):
+                gg = bn.group_rate([L2, L2], 1)
+                rows_out["gemv_group_gate_up_2x5504x2048_bf16_B1"] = {
+                    "ms": gg["grouped"], "separate_ms": gg["separate"],
+                    "packed_GB/s": 2 * L2["packed_bytes"] / (gg["grouped"] * 1e-3) / 1e9,
+                    "separate_packed_GB/s": 2 * L2["packed_bytes"] / (gg["separate"] * 1e-3) / 1e9}
             for bb in (1, 8):
                 msm = bn.gemv_rate(L2, d2, bb, F.FAIRY_BF16, steps=200)
                 rows_out[f"gemv_{name}_bf16_B{bb}"] = {
@@ -702,6 +814,15 @@ def full_layer_sweep(bn):
             out[f"layer_S{S}_B{B}"] = {"ms_total": tot_ms, "packed_bytes": tot_bytes,
                                         "packed_GB/s": tot_bytes / (tot_ms * 1e-3) / 1e9, "per_proj_ms": per}
             log(f"sweep S={S} B={B}: {tot_ms * 1e3:.1f} us, {tot_bytes / (tot_ms * 1e-3) / 1e9:.0f} GB/s")
+            # the whole layer as one step: seven launches, or four with q+k+v
+            # and gate+up grouped
+            for grouped in (False, True):
+                ms_l = bn.layer_step_rate(layers, B, grouped)
+                key = f"layer_step_S{S}_B{B}_{'grouped' if grouped else 'separate'}"
+                out[key] = {"ms": ms_l, "launches": 4 if grouped else 7,
+                            "packed_GB/s": tot_bytes / (ms_l * 1e-3) / 1e9}
+                log(f"sweep S={S} B={B} layer step ({'4 grouped' if grouped else '7'} launches): "
+                    f"{ms_l * 1e3:.1f} us, {tot_bytes / (ms_l * 1e-3) / 1e9:.0f} GB/s")
         del layers
         torch.cuda.empty_cache()
     # pure complex layers (no conjugate branch): per-component sigma 0.02

@@ -180,6 +180,27 @@ fairy_status fairy_cgemv(const fairy_clinear* L, const void* x_re, const void* x
     return from_hip(fairy::launch_cgemv(la, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, acc, as_stream(stream)));
 }
 
+fairy_status fairy_cgemv_group(const fairy_clinear* layers, int32_t count, const void* x_re, const void* x_im,
+                               int32_t xdtype, int32_t batch, int64_t ldx, float* const* y_re, float* const* y_im,
+                               const int64_t* ldy, void* stream)
+{
+    if (!layers || !y_re || !y_im || !ldy) return FAIRY_ERR_INVALID_ARG;
+    if (count < 1 || count > fairy::gemv::kMaxGroup) return FAIRY_ERR_INVALID_ARG;
+    if (batch < 1 || batch > 64) return FAIRY_ERR_INVALID_ARG;
+    fairy::LayerArgs la[fairy::gemv::kMaxGroup];
+    for (int32_t l = 0; l < count; ++l) {
+        fairy_status st = check_layer_call(&layers[l], x_re, x_im, xdtype, batch, ldx, y_re[l], y_im[l], ldy[l],
+                                           nullptr, &la[l]);
+        if (st != FAIRY_OK) return st;
+        if (layers[l].m != layers[0].m || layers[l].stages != layers[0].stages ||
+            layers[l].has_conj != layers[0].has_conj)
+            return FAIRY_ERR_INVALID_ARG;
+    }
+    clear_stale_error();
+    return from_hip(fairy::launch_cgemv_group(la, y_re, y_im, ldy, count, x_re, x_im, xdtype, batch, ldx,
+                                              as_stream(stream)));
+}
+
 // Layer view and block shape of a table-lookup GEMV call; false when the
 // layer is invalid or its chunk grid exceeds the launch limits.
 static bool lut_plan(const fairy_clinear* L, fairy::LayerArgs* la, fairy::LutConfig* c)

@@ -73,4 +73,45 @@ hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, 
     }
 }
 
+hipError_t launch_cgemv_group(const LayerArgs* L, const float* const* y_re, const float* const* y_im,
+                              const int64_t* ldy, int32_t count, const void* x_re, const void* x_im, int32_t xdtype,
+                              int64_t batch, int64_t ldx, hipStream_t s)
+{
+    // one launch when the shape takes the one-row-per-wave kernels, else
+    // one launch per layer
+    gemv::GemvArgs a = gemv::make_args(L[0], x_re, x_im, batch, ldx, const_cast<float*>(y_re[0]),
+                                       const_cast<float*>(y_im[0]), ldy[0], nullptr);
+    if (gemv::kScaleBytes + (size_t)gemv::x_bytes_per_col(xdtype, a.m64) > 64 * 1024) return hipErrorInvalidValue;
+    gemv::GroupTable gt{};
+    gt.count = count;
+    const int rows_pb = (xdtype == FAIRY_I8) ? 4 : 8;  // waves (rows) per block of the kernels below
+    int64_t blocks = 0;
+    for (int l = 0; l < count; ++l) {
+        gt.start[l] = (int32_t)blocks;
+        gt.packed[l] = L[l].packed;
+        gt.scales[l] = L[l].scales;
+        gt.y_re[l] = const_cast<float*>(y_re[l]);
+        gt.y_im[l] = const_cast<float*>(y_im[l]);
+        gt.ldy[l] = ldy[l];
+        gt.n[l] = (int32_t)L[l].n;
+        blocks += (L[l].n + rows_pb - 1) / rows_pb;
+    }
+    gt.start[count] = (int32_t)blocks;
+    hipError_t e = hipErrorNotSupported;
+    if (blocks < 0x7FFFFFFF) {
+        switch (xdtype) {
+        case FAIRY_BF16: e = gemv::launch_bf16_group(a, gt, s); break;
+        case FAIRY_F32: e = gemv::launch_f32_group(a, gt, s); break;
+        default: e = gemv::launch_i8_group(a, gt, s); break;
+        }
+    }
+    if (e != hipErrorNotSupported) return e;
+    for (int l = 0; l < count; ++l) {
+        e = launch_cgemv(L[l], x_re, x_im, xdtype, batch, ldx, const_cast<float*>(y_re[l]),
+                         const_cast<float*>(y_im[l]), ldy[l], nullptr, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace fairy

@@ -66,13 +66,13 @@ __device__ __forceinline__ void unit_i8(const uint4 cw, int g, const uint8_t* xs
 constexpr int kThreadsLpI8 = 256;
 
 template <int P, int BCH>
-__global__ __launch_bounds__(kThreadsLpI8) void k_cgemv_lp_i8(GemvArgs a)
+__device__ __forceinline__ void lp_i8_body(const GemvArgs& a, int blk)
 {
     static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "power-of-two plane count");
     constexpr int GS = 64 / P;  // groups one step of the wave covers
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * (kThreadsLpI8 / 64) + (threadIdx.x >> 6);
+    const int row = blk * (kThreadsLpI8 / 64) + (threadIdx.x >> 6);
     const bool row_ok = row < a.n;
     const int p = lane % P, gl = lane / P;
     const int G = a.G;
@@ -165,6 +165,38 @@ __global__ __launch_bounds__(kThreadsLpI8) void k_cgemv_lp_i8(GemvArgs a)
 }
 
 template <int P, int BCH>
+__global__ __launch_bounds__(kThreadsLpI8) void k_cgemv_lp_i8(GemvArgs a)
+{
+    lp_i8_body<P, BCH>(a, blockIdx.x);
+}
+
+template <int P, int BCH>
+__global__ __launch_bounds__(kThreadsLpI8) void k_cgemv_lp_i8_group(GemvArgs a, GroupTable gt)
+{
+    const int blk = group_resolve(gt, a, blockIdx.x);
+    lp_i8_body<P, BCH>(a, blk);
+}
+
+template <int P, int BCH>
+hipError_t launch_lp_i8_group_t(const GemvArgs& a, const GroupTable& gt, hipStream_t s)
+{
+    const dim3 grid(gt.start[gt.count], (a.B + BCH - 1) / BCH);
+    const size_t lds = (size_t)x_bytes_per_col(FAIRY_I8, a.m64) * BCH + 16;  // + the spare slot
+    hipLaunchKernelGGL((k_cgemv_lp_i8_group<P, BCH>), grid, dim3(kThreadsLpI8), lds, s, a, gt);
+    return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_lp_i8_group(const GemvArgs& a, const GroupTable& gt, hipStream_t s)
+{
+    switch (pick_bch_lp(FAIRY_I8, a.B, a.m64)) {
+    case 4: return launch_lp_i8_group_t<P, 4>(a, gt, s);
+    case 2: return launch_lp_i8_group_t<P, 2>(a, gt, s);
+    default: return launch_lp_i8_group_t<P, 1>(a, gt, s);
+    }
+}
+
+template <int P, int BCH>
 hipError_t launch_lp_i8_t(const GemvArgs& a, hipStream_t s)
 {
     const dim3 grid((a.n + (kThreadsLpI8 / 64) - 1) / (kThreadsLpI8 / 64), (a.B + BCH - 1) / BCH);
@@ -205,6 +237,20 @@ hipError_t launch_i8_p(const GemvArgs& a, int bch, hipStream_t s)
 }
 
 }  // namespace
+
+// grouped launch (no raw accumulators): power-of-two P on rows of >= 64 units
+hipError_t launch_i8_group(const GemvArgs& a, const GroupTable& gt, hipStream_t s)
+{
+    if (!(a.G * a.P >= 64 && a.B <= 64) || a.acc) return hipErrorNotSupported;
+    switch (a.P) {
+    case 1: return launch_lp_i8_group<1>(a, gt, s);
+    case 2: return launch_lp_i8_group<2>(a, gt, s);
+    case 4: return launch_lp_i8_group<4>(a, gt, s);
+    case 8: return launch_lp_i8_group<8>(a, gt, s);
+    case 16: return launch_lp_i8_group<16>(a, gt, s);
+    default: return hipErrorNotSupported;
+    }
+}
 
 hipError_t launch_i8(const GemvArgs& a, hipStream_t s)
 {

@@ -59,6 +59,40 @@ struct GemvArgs {
     double rope_log2_base;
 };
 
+// Several layers that read the same activations, in one launch (the q, k and
+// v projections of an attention layer, or gate and up of an MLP: [Fairy2i
+// article §2.2, item 1] each projection matrix gets its own widely-linear
+// form, all of them applied to the same input).  Blocks [start[l],
+// start[l+1]) of the grid belong to layer l; the layers share m, stages and
+// the conjugate branch, and keep their own rows, words, scales and outputs.
+constexpr int kMaxGroup = 8;
+struct GroupTable {
+    int32_t count;
+    int32_t start[kMaxGroup + 1];
+    const uint32_t* packed[kMaxGroup];
+    const float* scales[kMaxGroup];
+    float* y_re[kMaxGroup];
+    float* y_im[kMaxGroup];
+    int64_t ldy[kMaxGroup];
+    int32_t n[kMaxGroup];
+};
+
+// The layer of block `blk` (uniform; at most kMaxGroup - 1 comparisons):
+// its view of the arguments and the block number inside it.
+__device__ __forceinline__ int group_resolve(const GroupTable& gt, GemvArgs& a, int blk)
+{
+    int l = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGroup; ++i) l += (i < gt.count && blk >= gt.start[i]) ? 1 : 0;
+    a.packed = gt.packed[l];
+    a.scales = gt.scales[l];
+    a.y_re = gt.y_re[l];
+    a.y_im = gt.y_im[l];
+    a.ldy = gt.ldy[l];
+    a.n = gt.n[l];
+    return blk - gt.start[l];
+}
+
 // Complex rotary position encoding of an output [iFairy press article §三;
 // iFairy talk §2.1.3: on the complex plane the rotation is one complex
 // multiplication]: complex dimension j = row % rope_d of batch column (or
@@ -308,7 +342,7 @@ constexpr int kThreadsLp = 512;
 // blockIdx.y picks a chunk of BCH batch columns, so the chunks of a batch
 // run side by side (each re-reads the codes, from L2 after the first).
 template <int XT, int P, int BCH>
-__global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
+__device__ __forceinline__ void lp_body(const GemvArgs& a, int blk)
 {
     static_assert(P >= 1 && P <= 64, "plane count");
     constexpr int GS = 64 / P;  // groups one step of the wave covers
@@ -317,7 +351,7 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
     constexpr int per_elems = 16 / esize;
     extern __shared__ __align__(16) uint8_t lds[];
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * (kThreadsLp / 64) + (threadIdx.x >> 6);
+    const int row = blk * (kThreadsLp / 64) + (threadIdx.x >> 6);
     const bool row_ok = row < a.n;
     const int p = lane % P, gl = lane / P;
     // an idle lane must accumulate nothing (a zero code word decodes to +1)
@@ -414,6 +448,19 @@ __global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
             a.y_im[(int64_t)(b0 + b) * a.ldy + row] = vi;
         }
     }
+}
+
+template <int XT, int P, int BCH>
+__global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp(GemvArgs a)
+{
+    lp_body<XT, P, BCH>(a, blockIdx.x);
+}
+
+template <int XT, int P, int BCH>
+__global__ __launch_bounds__(kThreadsLp) void k_cgemv_lp_group(GemvArgs a, GroupTable gt)
+{
+    const int blk = group_resolve(gt, a, blockIdx.x);
+    lp_body<XT, P, BCH>(a, blk);
 }
 
 // ---------------------------------------------------------------------------
@@ -592,6 +639,26 @@ hipError_t launch_lp_bch(const GemvArgs& a, int bch, hipStream_t s)
     }
 }
 
+// grouped launch: gt.start[gt.count] blocks along x
+template <int XT, int P, int BCH>
+hipError_t launch_lp_group_t(const GemvArgs& a, const GroupTable& gt, hipStream_t s)
+{
+    const dim3 grid(gt.start[gt.count], (a.B + BCH - 1) / BCH);
+    const size_t lds = (size_t)x_bytes_per_col(XT, a.m64) * BCH + 16;  // + the spare slot
+    hipLaunchKernelGGL((k_cgemv_lp_group<XT, P, BCH>), grid, dim3(kThreadsLp), lds, s, a, gt);
+    return hipGetLastError();
+}
+
+template <int XT, int P>
+hipError_t launch_lp_group_bch(const GemvArgs& a, const GroupTable& gt, int bch, hipStream_t s)
+{
+    switch (bch) {
+    case 4: return launch_lp_group_t<XT, P, 4>(a, gt, s);
+    case 2: return launch_lp_group_t<XT, P, 2>(a, gt, s);
+    default: return launch_lp_group_t<XT, P, 1>(a, gt, s);
+    }
+}
+
 // Batch columns per block of the one-row-per-wave kernel: wide enough to
 // share each decoded word among a few columns, narrow enough that a small
 // layer still has several waves per SIMD (the chunks run side by side).
@@ -622,9 +689,32 @@ hipError_t launch_float(const GemvArgs& a, hipStream_t s)
     }
 }
 
+// One launch over the layers of gt (the one-row-per-wave kernels; P in
+// {1, 2, 3, 4, 6, 8, 16} and rows of >= 64 units): hipErrorNotSupported for
+// any other shape, which the caller then runs layer by layer.
+template <int XT>
+hipError_t launch_float_group(const GemvArgs& a, const GroupTable& gt, hipStream_t s)
+{
+    if (!(a.G * a.P >= 64 && a.B <= 64)) return hipErrorNotSupported;
+    const int bl = pick_bch_lp(XT, a.B, a.m64);
+    switch (a.P) {
+    case 1: return launch_lp_group_bch<XT, 1>(a, gt, bl, s);
+    case 2: return launch_lp_group_bch<XT, 2>(a, gt, bl, s);
+    case 3: return launch_lp_group_bch<XT, 3>(a, gt, bl, s);
+    case 4: return launch_lp_group_bch<XT, 4>(a, gt, bl, s);
+    case 6: return launch_lp_group_bch<XT, 6>(a, gt, bl, s);
+    case 8: return launch_lp_group_bch<XT, 8>(a, gt, bl, s);
+    case 16: return launch_lp_group_bch<XT, 16>(a, gt, bl, s);
+    default: return hipErrorNotSupported;
+    }
+}
+
 hipError_t launch_bf16(const GemvArgs& a, hipStream_t s);
 hipError_t launch_f32(const GemvArgs& a, hipStream_t s);
 hipError_t launch_i8(const GemvArgs& a, hipStream_t s);
+hipError_t launch_bf16_group(const GemvArgs& a, const GroupTable& gt, hipStream_t s);
+hipError_t launch_f32_group(const GemvArgs& a, const GroupTable& gt, hipStream_t s);
+hipError_t launch_i8_group(const GemvArgs& a, const GroupTable& gt, hipStream_t s);
 
 GemvArgs make_args(const LayerArgs& L, const void* x_re, const void* x_im, int64_t batch, int64_t ldx,
                    float* y_re, float* y_im, int64_t ldy, int32_t* acc);

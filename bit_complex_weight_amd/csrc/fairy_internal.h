@@ -146,6 +146,13 @@ hipError_t launch_cgemv(const LayerArgs& L, const void* x_re, const void* x_im, 
                         int64_t batch, int64_t ldx, float* y_re, float* y_im, int64_t ldy,
                         int32_t* acc, hipStream_t s);
 
+// Decode GEMV of up to 8 layers (same m, stages and conjugate branch) that
+// read the same activations: one launch when the shape allows, else one per
+// layer.  No raw accumulators, no rotary encoding.
+hipError_t launch_cgemv_group(const LayerArgs* L, const float* const* y_re, const float* const* y_im,
+                              const int64_t* ldy, int32_t count, const void* x_re, const void* x_im, int32_t xdtype,
+                              int64_t batch, int64_t ldx, hipStream_t s);
+
 // Whether fairy_cgemm takes the matrix-core path for these arguments (it
 // streams the activations in chunks, so any m; the VALU path stages whole
 // activation rows in LDS).

@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.fairy_cgemv.argtypes = [ctypes.POINTER(fairy_clinear), _p, _p, _i32, _i32, _i64, _p, _p, _i64, _p,
                                   _p, _sz, _p]
         L.fairy_cgemv.restype = _i32
+        L.fairy_cgemv_group.argtypes = [ctypes.POINTER(fairy_clinear), _i32, _p, _p, _i32, _i32, _i64, _p, _p, _p, _p]
+        L.fairy_cgemv_group.restype = _i32
         L.fairy_cgemm_workspace_bytes.argtypes = [ctypes.POINTER(fairy_clinear), _i64, _i32, _i32]
         L.fairy_cgemm_workspace_bytes.restype = _sz
         L.fairy_cgemm.argtypes = [ctypes.POINTER(fairy_clinear), _p, _p, _i32, _i64, _i64, _p, _p, _i64, _p,
@@ -218,6 +220,20 @@ def fairy_cgemv(L, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, acc=None, wo
                 workspace_bytes=0, stream=None):
     _check(lib().fairy_cgemv(ctypes.byref(L), _ptr(x_re), _ptr(x_im), xdtype, batch, ldx, _ptr(y_re), _ptr(y_im),
                              ldy, _ptr(acc), _ptr(workspace), workspace_bytes, _stream(stream)), "fairy_cgemv")
+
+
+def fairy_cgemv_group(layers, x_re, x_im, xdtype, batch, ldx, y_re, y_im, ldy, stream=None):
+    """layers, y_re, y_im, ldy: sequences of the same length (descriptors,
+    device buffers, leading dimensions)."""
+    k = len(layers)
+    if not (len(y_re) == len(y_im) == len(ldy) == k):
+        raise ValueError("fairy_cgemv_group: layers, y_re, y_im and ldy differ in length")
+    arr = (fairy_clinear * k)(*layers)
+    yr = (_p * k)(*[_ptr(v) for v in y_re])
+    yi = (_p * k)(*[_ptr(v) for v in y_im])
+    ld = (_i64 * k)(*[int(v) for v in ldy])
+    _check(lib().fairy_cgemv_group(arr, k, _ptr(x_re), _ptr(x_im), xdtype, batch, ldx, ctypes.cast(yr, _p),
+                                   ctypes.cast(yi, _p), ctypes.cast(ld, _p), _stream(stream)), "fairy_cgemv_group")
 
 
 def fairy_cgemm_workspace_bytes(L, M, xdtype, algo) -> int:

@@ -203,6 +203,26 @@ fairy_status fairy_cgemv(const fairy_clinear* L, const void* x_re, const void* x
                          float* y_re, float* y_im, int64_t ldy, int32_t* acc,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Several layers on one input ------------------------------------------------
+ * [Fairy2i article §2.2, item 1: every projection matrix of an attention
+ * layer (Q, K and V) gets its own widely-linear form, and all of them are
+ * applied to the same input]  fairy_cgemv for `count` layers that read the
+ * same activations, in one launch where the shape allows (the q, k and v
+ * projections, or gate and up of an MLP), else layer by layer.  Each output
+ * equals what fairy_cgemv gives for that layer alone (same kernels and
+ * summation order).
+ *   layers     : host array [count] (1 <= count <= 8) of descriptors, each
+ *                valid for fairy_cgemv; all with the same m, stages and
+ *                has_conj (else INVALID_ARG); n may differ.
+ *   x_re, x_im : as fairy_cgemv, shared by every layer.
+ *   y_re, y_im : host arrays [count] of device pointers, layer l writes
+ *                [batch][ldy[l]] fp32 there; ldy: host array [count].
+ *   batch      : 1..64.  No raw accumulators.
+ * Same float bound as fairy_cgemv. */
+fairy_status fairy_cgemv_group(const fairy_clinear* layers, int32_t count, const void* x_re, const void* x_im,
+                               int32_t xdtype, int32_t batch, int64_t ldx, float* const* y_re, float* const* y_im,
+                               const int64_t* ldy, void* stream);
+
 /* ---- Table-lookup GEMV (batch 1) ----------------------------------------------
  * [iFairy talk §2.3.2: table-lookup inference precomputes the results of the
  * 16 input combinations of a pair of codes]  Same result as fairy_cgemv with

@@ -246,3 +246,40 @@ def test_python_binding_rejects_host_buffers():
     import numpy as np
     with pytest.raises(TypeError):
         F._ptr(np.zeros(4))
+
+
+def test_cgemv_group_validation():
+    """Grouped GEMV: 1..8 layers sharing m, stages and the conjugate branch;
+    every layer checked as fairy_cgemv checks it; host arrays required."""
+    f = L_.fairy_cgemv_group
+    P = ctypes.c_void_p
+
+    def call(layers, batch=1, ldy=None, yr=None, yi=None, dt=F.FAIRY_BF16, ldx=2048):
+        k = len(layers)
+        arr = (F.fairy_clinear * max(k, 1))(*layers) if k else None
+        yr = yr if yr is not None else (P * max(k, 1))(*([A] * max(k, 1)))
+        yi = yi if yi is not None else (P * max(k, 1))(*([A] * max(k, 1)))
+        ld = ldy if ldy is not None else (ctypes.c_int64 * max(k, 1))(*[l.n for l in layers] or [1])
+        return f(arr, k, A, A, dt, batch, ldx, ctypes.cast(yr, P) if yr else None,
+                 ctypes.cast(yi, P) if yi else None, ctypes.cast(ld, P) if ld else None, None)
+
+    q = F.make_clinear(2048, 2048, 2, 1, A, A)
+    gate = F.make_clinear(5504, 2048, 2, 1, A, A)
+    assert call([]) == F.FAIRY_ERR_INVALID_ARG                          # count 0
+    assert call([q] * 9) == F.FAIRY_ERR_INVALID_ARG                     # count > 8
+    assert call([q, gate], batch=0) == F.FAIRY_ERR_INVALID_ARG
+    assert call([q, gate], batch=65) == F.FAIRY_ERR_INVALID_ARG
+    assert call([q, F.make_clinear(2048, 4096, 2, 1, A, A)]) == F.FAIRY_ERR_INVALID_ARG   # m differs
+    assert call([q, F.make_clinear(2048, 2048, 1, 1, A, A)]) == F.FAIRY_ERR_INVALID_ARG   # stages differ
+    assert call([q, F.make_clinear(2048, 2048, 2, 0, A, A)]) == F.FAIRY_ERR_INVALID_ARG   # conj differs
+    assert call([q, F.make_clinear(2048, 2048, 2, 1, A + 4, A)]) == F.FAIRY_ERR_INVALID_ARG  # misaligned words
+    assert call([q, q], ldy=(ctypes.c_int64 * 2)(2048, 2047)) == F.FAIRY_ERR_INVALID_ARG    # ldy < n
+    assert call([q, q], yr=(P * 2)(A, None)) == F.FAIRY_ERR_INVALID_ARG                    # null output
+    assert f(None, 1, A, A, F.FAIRY_BF16, 1, 2048, A, A, A, None) == F.FAIRY_ERR_INVALID_ARG
+    arr = (F.fairy_clinear * 1)(q)
+    assert f(arr, 1, A, A, F.FAIRY_BF16, 1, 2048, None, A, A, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(arr, 1, A, A, F.FAIRY_BF16, 1, 2048, A, A, None, None) == F.FAIRY_ERR_INVALID_ARG
+    # same width rules as fairy_cgemv: m % 16, the staged-activation limit
+    assert call([F.make_clinear(64, 24, 1, 0, A, A)], ldx=32) == F.FAIRY_ERR_UNSUPPORTED
+    wide = F.make_clinear(64, 16384, 1, 0, A, A)
+    assert call([wide], ldx=16384) == F.FAIRY_ERR_UNSUPPORTED
