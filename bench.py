@@ -179,6 +179,19 @@ class Bench:
 
         return launch, elapsed_ms, cleanup
 
+    def graph_ms(self, fn, steps):
+        """ms per call of fn(i) over `steps` calls captured as one HIP graph,
+        timed between the graph's event nodes on a replay after one untimed
+        replay (launch overhead of the Python binding excluded)."""
+        st = self.torch.cuda.Stream()
+        launch, elapsed_ms, cleanup = self.timed_graph(fn, steps, st)
+        launch()
+        launch()
+        st.synchronize()
+        ms = elapsed_ms() / steps
+        cleanup()
+        return ms
+
     def cold_runs(self, make_fn, steps, ncopy, flush):
         """Timed runs of exactly `steps` launches each, every run on cold
         weights.  Run r captures the launches make_fn(r*steps + j) (j <
@@ -448,6 +461,8 @@ def main():
     ap.add_argument("--layer", action="store_true",
                     help="only time the whole S=2 layer step (7 projections, batch 1 and 4) as 7 launches and as "
                          "4 with the grouped GEMV, e.g. under a profiler")
+    ap.add_argument("--quant", action="store_true",
+                    help="only time PhaseQuant (S=2) and pack on the 2048x2048 layer, e.g. under a profiler")
     ap.add_argument("--calib", action="store_true",
                     help="only measure the ceilings: a plain 256 MiB copy (the byte-counter calibration "
                          "kernel), 4 MiB and 32 MiB copy launches and tiny launches in HIP graphs")
@@ -475,6 +490,17 @@ def main():
         ms_l = bn.lut_rate(L, descs, steps=args.steps)
         ms_d = bn.gemv_rate(L, descs, 1, F.FAIRY_BF16, steps=args.steps)
         print(json.dumps({"gemv_lut_2048x2048_bf16_B1": lut_entry(ms_l, ms_d, L)}), flush=True)
+        return
+    if args.quant:
+        L = bn.widely_linear_layer(4096, 4096, 2, seed=200)
+        n, m, S, P = L["n"], L["m"], L["S"], L["P"]
+        pl, cd, sc, ws, wsb = L["planes"], L["codes"], L["scales"], L["ws"], L["wsb"]
+        ms_q = bn.graph_ms(lambda i: F.fairy_phasequant(pl[0], pl[1], L["count"], S, cd[0], sc[0], None, None, ws,
+                                                        wsb), args.steps)
+        ms_p = bn.graph_ms(lambda i: F.fairy_pack(cd, P, n, m, F.FAIRY_LAYOUT_TILED64, L["packed"]), args.steps)
+        print(json.dumps({"phasequant_S2_2048x2048": {"ms": ms_q, "unique_GB/s": (L["count"] * 8) / (ms_q * 1e-3) / 1e9},
+                          "pack_P4_2048x2048": {"ms": ms_p, "GB/s": (P * L["count"] * 1.25) / (ms_p * 1e-3) / 1e9}}),
+              flush=True)
         return
     if args.layer:
         proj = {"q": (4096, 4096), "k": (4096, 4096), "v": (4096, 4096), "o": (4096, 4096),
@@ -610,18 +636,18 @@ def main():
         rows_out = {}
         R, planes, codes, scales, ws, wsb = L["R"], L["planes"], L["codes"], L["scales"], L["ws"], L["wsb"]
         count = L["count"]
-        ms_c = bn.ev_time(lambda i: F.fairy_real_to_complex(R, n, m, *planes), 20)
+        ms_c = bn.graph_ms(lambda i: F.fairy_real_to_complex(R, n, m, *planes), 20)
         rows_out["real_to_complex_4096x4096"] = {"ms": ms_c, "GB/s": (4 * 4 * n * m * 2) / (ms_c * 1e-3) / 1e9}
-        ms_q = bn.ev_time(lambda i: F.fairy_phasequant(planes[0], planes[1], count, S, codes[0], scales[0], None,
-                                                       None, ws, wsb), 20)
+        ms_q = bn.graph_ms(lambda i: F.fairy_phasequant(planes[0], planes[1], count, S, codes[0], scales[0], None,
+                                                        None, ws, wsb), 20)
         rows_out["phasequant_S2_2048x2048"] = {"ms": ms_q, "unique_GB/s": (count * 8) / (ms_q * 1e-3) / 1e9}
-        ms_p = bn.ev_time(lambda i: F.fairy_pack(codes, P, n, m, F.FAIRY_LAYOUT_TILED64, L["packed"]), 20)
+        ms_p = bn.graph_ms(lambda i: F.fairy_pack(codes, P, n, m, F.FAIRY_LAYOUT_TILED64, L["packed"]), 20)
         rows_out["pack_P4_2048x2048"] = {"ms": ms_p, "GB/s": (P * count * 1.25) / (ms_p * 1e-3) / 1e9}
         # the whole conversion (split, PhaseQuant of U and W, pack) in one call
         q_packed, q_scales = torch.empty_like(L["packed"]), torch.empty_like(L["scales"])
         wsq = F.fairy_quantize_workspace_bytes(n, m, S, 1)
         wq = torch.empty(wsq, dtype=torch.uint8, device="cuda")
-        ms_r = bn.ev_time(lambda i: F.fairy_quantize_real(R, n, m, S, q_packed, q_scales, wq, wsq), 10)
+        ms_r = bn.graph_ms(lambda i: F.fairy_quantize_real(R, n, m, S, q_packed, q_scales, wq, wsq), 10)
         if not (torch.equal(q_packed, L["packed"]) and torch.equal(q_scales, L["scales"])):
             raise SystemExit("fairy_quantize_real differs from the step-by-step conversion")
         rows_out["quantize_real_4096x4096_S2"] = {"ms": ms_r, "R_GB/s": (4 * n * m * 4) / (ms_r * 1e-3) / 1e9}

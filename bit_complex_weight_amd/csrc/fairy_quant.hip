@@ -85,22 +85,30 @@ __global__ __launch_bounds__(kThreads) void k_real_to_complex1(const float* __re
 // Quadrant of arg(a + ib) by exact comparisons: floor(2 theta/pi + 1/2) mod 4;
 // on |a| == |b| the floor sends theta = 45, 135, -135, -45 degrees to
 // codes 1, 2, 3, 0; zero (either sign) -> 0.
+// Written with selects only: a branch per element would diverge inside the
+// wave and cost scalar exec-mask instructions around every comparison.
 __device__ __forceinline__ uint32_t phase_code(float a, float b)
 {
     const float A = fabsf(a), B = fabsf(b);
-    if (A > B) return a > 0.0f ? 0u : 2u;
-    if (B > A) return b > 0.0f ? 1u : 3u;
-    if (A == 0.0f) return 0u;
-    return a > 0.0f ? (b > 0.0f ? 1u : 0u) : (b > 0.0f ? 2u : 3u);
+    const uint32_t c_re = a > 0.0f ? 0u : 2u;                                 // |a| > |b|
+    const uint32_t c_im = b > 0.0f ? 1u : 3u;                                 // |b| > |a|
+    const uint32_t c_tie = a > 0.0f ? (b > 0.0f ? 1u : 0u) : (b > 0.0f ? 2u : 3u);
+    const uint32_t c_eq = (A == 0.0f) ? 0u : c_tie;
+    return (A > B) ? c_re : ((B > A) ? c_im : c_eq);
 }
 
-// R <- R - (s_re Re(i^c) + i s_im Im(i^c)), one fp32 operation on the code's axis.
+// R <- R - (s_re Re(i^c) + i s_im Im(i^c)), one fp32 operation on the code's
+// axis: codes 0 / 1 subtract the scale, codes 2 / 3 subtract its negation
+// (x - (-s) is the same IEEE operation as x + s).
 __device__ __forceinline__ void residual_step(float& a, float& b, uint32_t c, float s_re, float s_im)
 {
-    if (c == 0u) a = a - s_re;
-    else if (c == 2u) a = a + s_re;
-    else if (c == 1u) b = b - s_im;
-    else b = b + s_im;
+    const bool neg = (c & 2u) != 0u;
+    const float dr = neg ? -s_re : s_re;
+    const float di = neg ? -s_im : s_im;
+    const bool re_axis = (c & 1u) == 0u;
+    const float na = a - dr, nb = b - di;
+    a = re_axis ? na : a;
+    b = re_axis ? b : nb;
 }
 
 // Workspace per stage: 2 axes x 256 exponent buckets (uint64) + 2 counts.
@@ -148,44 +156,65 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
     if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0ull;
     __syncthreads();
 
+    // the scales of the earlier stages, read once (uniform values; the
+    // residual loop below is unrolled, so none is indexed at run time)
     float sre[8], sim[8];
-    for (int j = 0; j < k; ++j) {
-        sre[j] = scales[2 * j];
-        sim[j] = scales[2 * j + 1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        sre[j] = (j < k) ? scales[2 * j] : 0.0f;
+        sim[j] = (j < k) ? scales[2 * j + 1] : 0.0f;
     }
     const int copy = threadIdx.x % kCopies;
     const int64_t nv = count / V;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const vec_t* vr = reinterpret_cast<const vec_t*>(w_re);
     const vec_t* vi = reinterpret_cast<const vec_t*>(w_im);
     code_t* cout = reinterpret_cast<code_t*>(codes + (int64_t)k * count);
     uint32_t n_im = 0, n_all = 0;
-    for (int64_t iv = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; iv < nv;
-         iv += (int64_t)gridDim.x * blockDim.x) {
-        const vec_t ra = vr[iv], rb = vi[iv];
-        float av[V], bv[V];
-        if constexpr (V == 4) {
-            av[0] = ra.x; av[1] = ra.y; av[2] = ra.z; av[3] = ra.w;
-            bv[0] = rb.x; bv[1] = rb.y; bv[2] = rb.z; bv[3] = rb.w;
-        } else {
-            av[0] = ra;
-            bv[0] = rb;
-        }
-        uint32_t cpack = 0;
+    // kUnroll grid-stride steps at a time: all their loads are issued before
+    // any of them is processed
+    constexpr int kUnroll = 4;
+    for (int64_t iv0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; iv0 < nv; iv0 += kUnroll * stride) {
+        vec_t ra[kUnroll], rb[kUnroll];
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            float a = av[e], b = bv[e];
-            for (int j = 0; j < k; ++j) residual_step(a, b, phase_code(a, b), sre[j], sim[j]);
-            const uint32_t c = phase_code(a, b);
-            cpack |= c << (8 * e);
-            const uint32_t axis = c & 1u;
-            n_im += axis;
-            const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
-            const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
-            const uint32_t sig = ex ? (man | 0x800000u) : man;
-            if (sig) atomicAdd(&s_buck[(axis * 256u + (ex ? ex : 1u)) * kCopies + copy], (unsigned long long)sig);
+        for (int q = 0; q < kUnroll; ++q) {
+            const int64_t iv = iv0 + q * stride;
+            const int64_t il = iv < nv ? iv : iv0;  // a step past the end reloads the first (not processed)
+            ra[q] = vr[il];
+            rb[q] = vi[il];
         }
-        n_all += V;
-        cout[iv] = (code_t)cpack;
+#pragma unroll
+        for (int q = 0; q < kUnroll; ++q) {
+            const int64_t iv = iv0 + q * stride;
+            if (iv >= nv) break;
+            float av[V], bv[V];
+            if constexpr (V == 4) {
+                av[0] = ra[q].x; av[1] = ra[q].y; av[2] = ra[q].z; av[3] = ra[q].w;
+                bv[0] = rb[q].x; bv[1] = rb[q].y; bv[2] = rb[q].z; bv[3] = rb[q].w;
+            } else {
+                av[0] = ra[q];
+                bv[0] = rb[q];
+            }
+            uint32_t cpack = 0;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float a = av[e], b = bv[e];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (j < k) residual_step(a, b, phase_code(a, b), sre[j], sim[j]);
+                const uint32_t c = phase_code(a, b);
+                cpack |= c << (8 * e);
+                const uint32_t axis = c & 1u;
+                n_im += axis;
+                const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
+                const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
+                const uint32_t sig = ex ? (man | 0x800000u) : man;
+                // unconditional (adding 0 for a zero magnitude changes nothing)
+                atomicAdd(&s_buck[(axis * 256u + (ex ? ex : 1u)) * kCopies + copy], (unsigned long long)sig);
+            }
+            n_all += V;
+            cout[iv] = (code_t)cpack;
+        }
     }
     if (n_all - n_im) atomicAdd(&s_cnt[0], (unsigned long long)(n_all - n_im));
     if (n_im) atomicAdd(&s_cnt[1], (unsigned long long)n_im);
@@ -360,75 +389,98 @@ __device__ __forceinline__ void load16(const uint8_t* p, uint8_t out[16])
     for (int t = 0; t < 16; ++t) out[t] = (uint8_t)(w[t >> 2] >> (8 * (t & 3)));
 }
 
-__global__ __launch_bounds__(kThreads) void k_pack(const uint8_t* __restrict__ codes, int32_t planes,
-                                                   int64_t rows, int64_t m, int32_t layout,
-                                                   uint32_t* __restrict__ out, int64_t nwords)
+// ROW16: one thread per output word (consecutive threads, consecutive words
+// of one plane row: coalesced both ways).
+__global__ __launch_bounds__(kThreads) void k_pack_row16(const uint8_t* __restrict__ codes,
+                                                         uint32_t* __restrict__ out, int64_t nwords)
 {
-    const int64_t G = (m + 63) / 64;
     for (int64_t wi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; wi < nwords;
          wi += (int64_t)gridDim.x * blockDim.x) {
-        int64_t p, r, c0;
-        if (layout == FAIRY_LAYOUT_ROW16) {
-            const int64_t wpr = m / 16;
-            const int64_t pr = wi / wpr;
-            c0 = (wi - pr * wpr) * 16;
-            p = pr / rows;
-            r = pr - p * rows;
-        } else {
-            const int64_t u = wi & 3;
-            const int64_t q = wi >> 2;
-            p = q % planes;
-            const int64_t rg = q / planes;
-            const int64_t g = rg % G;
-            r = rg / G;
-            c0 = 64 * g + 16 * u;
-        }
+        // word wi covers codes 16 wi .. 16 wi + 15 of the [planes][rows][m] array
+        uint8_t c[16];
+        load16(codes + 16 * wi, c);
         uint32_t word = 0u;
-        if (c0 < m) {
-            uint8_t c[16];
-            load16(codes + (p * rows + r) * m + c0, c);
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const uint32_t bitpos = (layout == FAIRY_LAYOUT_ROW16) ? (uint32_t)(2 * t) : tiled_bit(t);
-                word |= ((uint32_t)c[t] & 3u) << bitpos;
-            }
-        }
+        for (int t = 0; t < 16; ++t) word |= ((uint32_t)c[t] & 3u) << (2 * t);
         out[wi] = word;
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_unpack(const uint32_t* __restrict__ in, int32_t planes,
-                                                     int64_t rows, int64_t m, int32_t layout,
-                                                     uint8_t* __restrict__ codes, int64_t nwords)
+__global__ __launch_bounds__(kThreads) void k_unpack_row16(const uint32_t* __restrict__ in,
+                                                           uint8_t* __restrict__ codes, int64_t nwords)
 {
-    const int64_t G = (m + 63) / 64;
     for (int64_t wi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; wi < nwords;
          wi += (int64_t)gridDim.x * blockDim.x) {
-        int64_t p, r, c0;
-        if (layout == FAIRY_LAYOUT_ROW16) {
-            const int64_t wpr = m / 16;
-            const int64_t pr = wi / wpr;
-            c0 = (wi - pr * wpr) * 16;
-            p = pr / rows;
-            r = pr - p * rows;
-        } else {
-            const int64_t u = wi & 3;
-            const int64_t q = wi >> 2;
-            p = q % planes;
-            const int64_t rg = q / planes;
-            const int64_t g = rg % G;
-            r = rg / G;
-            c0 = 64 * g + 16 * u;
-        }
-        if (c0 >= m) continue;
         const uint32_t word = in[wi];
         uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const uint32_t bitpos = (layout == FAIRY_LAYOUT_ROW16) ? (uint32_t)(2 * t) : tiled_bit(t);
-            o[t >> 2] |= ((word >> bitpos) & 3u) << (8 * (t & 3));
+        for (int t = 0; t < 16; ++t) o[t >> 2] |= ((word >> (2 * t)) & 3u) << (8 * (t & 3));
+        *reinterpret_cast<uint4*>(codes + 16 * wi) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// TILED64, one thread per (row, 64-column group): for every plane it reads
+// the group's 64 codes (64 contiguous bytes; consecutive threads take
+// consecutive groups of a row, so a wave reads contiguous kilobytes) and
+// writes that plane's 16-byte unit; the P units of (row, group) are
+// contiguous, so consecutive planes complete the same lines.
+__device__ __forceinline__ uint32_t pack_word16(const uint4 v)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t word = 0u;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) word |= ((w[t >> 2] >> (8 * (t & 3))) & 3u) << tiled_bit(t);
+    return word;
+}
+
+__global__ __launch_bounds__(kThreads) void k_pack_tiled(const uint8_t* __restrict__ codes, int32_t planes,
+                                                         int64_t rows, int64_t m, uint32_t* __restrict__ out)
+{
+    const int64_t G = (m + 63) / 64;
+    const int64_t units = rows * G;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < units;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / G, g = i - r * G;
+        const int64_t c0 = 64 * g;
+        const int nw = (m - c0) >= 64 ? 4 : (int)((m - c0) >> 4);  // valid 16-column words
+        for (int p = 0; p < planes; ++p) {
+            const uint4* src = reinterpret_cast<const uint4*>(codes + ((int64_t)p * rows + r) * m + c0);
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = (u < nw) ? src[u] : make_uint4(0, 0, 0, 0);
+            uint4 o;
+            o.x = pack_word16(v[0]);
+            o.y = pack_word16(v[1]);
+            o.z = pack_word16(v[2]);
+            o.w = pack_word16(v[3]);
+            reinterpret_cast<uint4*>(out)[(i * planes + p)] = o;
         }
-        *reinterpret_cast<uint4*>(codes + (p * rows + r) * m + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_unpack_tiled(const uint32_t* __restrict__ in, int32_t planes,
+                                                           int64_t rows, int64_t m, uint8_t* __restrict__ codes)
+{
+    const int64_t G = (m + 63) / 64;
+    const int64_t units = rows * G;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < units;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / G, g = i - r * G;
+        const int64_t c0 = 64 * g;
+        const int nw = (m - c0) >= 64 ? 4 : (int)((m - c0) >> 4);
+        for (int p = 0; p < planes; ++p) {
+            const uint4 wv = reinterpret_cast<const uint4*>(in)[i * planes + p];
+            const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+            uint4* dst = reinterpret_cast<uint4*>(codes + ((int64_t)p * rows + r) * m + c0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (u >= nw) break;
+                uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int t = 0; t < 16; ++t) o[t >> 2] |= ((words[u] >> tiled_bit(t)) & 3u) << (8 * (t & 3));
+                dst[u] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
     }
 }
 
@@ -496,18 +548,28 @@ int64_t packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout)
 hipError_t launch_pack(const uint8_t* codes, int32_t planes, int64_t rows, int64_t m, int32_t layout,
                        uint32_t* packed, hipStream_t s)
 {
+    if (layout == FAIRY_LAYOUT_TILED64) {
+        const int64_t units = rows * ((m + 63) / 64);
+        hipLaunchKernelGGL(k_pack_tiled, dim3(grid_for(units, kThreads, 16384)), dim3(kThreads), 0, s, codes, planes,
+                           rows, m, packed);
+        return hipGetLastError();
+    }
     const int64_t nw = packed_words(rows, m, planes, layout);
-    hipLaunchKernelGGL(k_pack, dim3(grid_for(nw, kThreads, 8192)), dim3(kThreads), 0, s, codes, planes, rows,
-                       m, layout, packed, nw);
+    hipLaunchKernelGGL(k_pack_row16, dim3(grid_for(nw, kThreads, 8192)), dim3(kThreads), 0, s, codes, packed, nw);
     return hipGetLastError();
 }
 
 hipError_t launch_unpack(const uint32_t* packed, int32_t planes, int64_t rows, int64_t m, int32_t layout,
                          uint8_t* codes, hipStream_t s)
 {
+    if (layout == FAIRY_LAYOUT_TILED64) {
+        const int64_t units = rows * ((m + 63) / 64);
+        hipLaunchKernelGGL(k_unpack_tiled, dim3(grid_for(units, kThreads, 16384)), dim3(kThreads), 0, s, packed,
+                           planes, rows, m, codes);
+        return hipGetLastError();
+    }
     const int64_t nw = packed_words(rows, m, planes, layout);
-    hipLaunchKernelGGL(k_unpack, dim3(grid_for(nw, kThreads, 8192)), dim3(kThreads), 0, s, packed, planes,
-                       rows, m, layout, codes, nw);
+    hipLaunchKernelGGL(k_unpack_row16, dim3(grid_for(nw, kThreads, 8192)), dim3(kThreads), 0, s, packed, codes, nw);
     return hipGetLastError();
 }
 
