@@ -120,6 +120,24 @@ fairy_status fairy_phasequant(const float* w_re, const float* w_im, int64_t coun
                                              workspace, as_stream(stream)));
 }
 
+fairy_status fairy_phasequant_noalloc(const float* w_re, const float* w_im, int64_t count, int32_t stages,
+                                      uint8_t* codes, float* scales, float* resid_re, float* resid_im, void* stream)
+{
+    if (!w_re || !w_im || !codes || !scales) return FAIRY_ERR_INVALID_ARG;
+    if (count < 1 || count >= ((int64_t)1 << 32)) return FAIRY_ERR_INVALID_ARG;
+    if (stages < 1 || stages > 8) return FAIRY_ERR_INVALID_ARG;
+    if (!aligned(w_re, 4) || !aligned(w_im, 4) || !aligned(scales, 4) || (resid_re && !aligned(resid_re, 4)) ||
+        (resid_im && !aligned(resid_im, 4)))
+        return FAIRY_ERR_INVALID_ARG;
+    if (fairy::phasequant_workspace_bytes(stages) > fairy::phasequant_scratch_bytes()) return FAIRY_ERR_UNSUPPORTED;
+    clear_stale_error();
+    void* ws = nullptr;
+    hipError_t e = fairy::phasequant_scratch(&ws);
+    if (e != hipSuccess) return FAIRY_ERR_HIP;
+    return from_hip(fairy::launch_phasequant(w_re, w_im, count, stages, codes, scales, resid_re, resid_im, ws,
+                                             as_stream(stream)));
+}
+
 int64_t fairy_packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout)
 {
     if (rows < 1 || m < 1 || planes < 1 || planes > 16 || !valid_layout(layout)) return -1;

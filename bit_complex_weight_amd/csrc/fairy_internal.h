@@ -125,6 +125,11 @@ hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count
                              uint8_t* codes, float* scales, float* resid_re, float* resid_im,
                              void* workspace, hipStream_t s);
 
+// Device address (current device) and size of the static PhaseQuant bucket
+// array used by fairy_phasequant_noalloc.
+hipError_t phasequant_scratch(void** out);
+size_t phasequant_scratch_bytes();
+
 int64_t packed_words(int64_t rows, int64_t m, int32_t planes, int32_t layout);
 hipError_t launch_pack(const uint8_t* codes, int32_t planes, int64_t rows, int64_t m, int32_t layout,
                        uint32_t* packed, hipStream_t s);

@@ -7,6 +7,7 @@
 // stream and allocate nothing.
 #include "fairy_internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace fairy {
@@ -536,6 +537,43 @@ hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count
                            (const float*)scales, resid_re, resid_im);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// PhaseQuant without a caller workspace: the exponent buckets live in this
+// file-scope device array, sized for the most stages a call may ask for.
+// Each GPU holds its own copy until the process ends.  Host code never uses
+// the array's name as a device address: its address on the current device
+// comes from hipGetSymbolAddress, once per device, and that pointer is what
+// the kernels receive.  Every call clears the buckets it uses (a fill kernel,
+// not a memset) before the first stage, so the array's previous contents do
+// not matter; calls that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+constexpr size_t kPqScratchBytes = (size_t)8 * kGlobalCopies * kStageWords * sizeof(unsigned long long);
+static __device__ __align__(256) unsigned char scratch[kPqScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+size_t phasequant_scratch_bytes() { return kPqScratchBytes; }
+
+hipError_t phasequant_scratch(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return hipSuccess;
 }
 

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.fairy_phasequant_workspace_bytes.restype = _sz
         L.fairy_phasequant.argtypes = [_p, _p, _i64, _i32, _p, _p, _p, _p, _p, _sz, _p]
         L.fairy_phasequant.restype = _i32
+        L.fairy_phasequant_noalloc.argtypes = [_p, _p, _i64, _i32, _p, _p, _p, _p, _p]
+        L.fairy_phasequant_noalloc.restype = _i32
         L.fairy_packed_words.argtypes = [_i64, _i64, _i32, _i32]
         L.fairy_packed_words.restype = _i64
         L.fairy_pack.argtypes = [_p, _i32, _i64, _i64, _i32, _p, _p]
@@ -192,6 +194,12 @@ def fairy_phasequant(w_re, w_im, count, stages, codes, scales, resid_re, resid_i
     _check(lib().fairy_phasequant(_ptr(w_re), _ptr(w_im), count, stages, _ptr(codes), _ptr(scales),
                                   _ptr(resid_re), _ptr(resid_im), _ptr(workspace), workspace_bytes,
                                   _stream(stream)), "fairy_phasequant")
+
+
+def fairy_phasequant_noalloc(w_re, w_im, count, stages, codes, scales, resid_re=None, resid_im=None, stream=None):
+    _check(lib().fairy_phasequant_noalloc(_ptr(w_re), _ptr(w_im), count, stages, _ptr(codes), _ptr(scales),
+                                          _ptr(resid_re), _ptr(resid_im), _stream(stream)),
+           "fairy_phasequant_noalloc")
 
 
 def fairy_packed_words(rows, m, planes, layout) -> int:

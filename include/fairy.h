@@ -157,6 +157,20 @@ fairy_status fairy_phasequant(const float* w_re, const float* w_im, int64_t coun
                               uint8_t* codes, float* scales, float* resid_re, float* resid_im,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* PhaseQuant for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): fairy_phasequant
+ * with the same arguments except the workspace, and the same kernels and
+ * results bit for bit.  The exponent buckets live in a static device array
+ * inside the library, 526,336 bytes (8 stages x 65,792), which each GPU the
+ * library runs on holds until the process ends; every valid stage count
+ * fits (otherwise UNSUPPORTED).  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); its first call on a device looks up the
+ * array's address there.  All calls on one GPU share that array: calls that
+ * overlap on one GPU (on different streams) race and must not be issued. */
+fairy_status fairy_phasequant_noalloc(const float* w_re, const float* w_im, int64_t count, int32_t stages,
+                                      uint8_t* codes, float* scales, float* resid_re, float* resid_im,
+                                      void* stream);
+
 /* ---- Packed storage ------------------------------------------------------------
  * [iFairy press article §一: a weight takes two bits, so a model takes one
  * eighth of its fp16 storage; Fairy2i article §5.2 item 3: the device must

@@ -283,3 +283,20 @@ def test_cgemv_group_validation():
     assert call([F.make_clinear(64, 24, 1, 0, A, A)], ldx=32) == F.FAIRY_ERR_UNSUPPORTED
     wide = F.make_clinear(64, 16384, 1, 0, A, A)
     assert call([wide], ldx=16384) == F.FAIRY_ERR_UNSUPPORTED
+
+
+def test_phasequant_noalloc_validation():
+    """The allocation-free PhaseQuant checks its arguments as fairy_phasequant
+    does (no workspace argument) before any HIP call."""
+    f = L_.fairy_phasequant_noalloc
+    assert f(None, A, 100, 2, A, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, None, 100, 2, A, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 2, None, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 2, A, None, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 0, 2, A, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 1 << 32, 2, A, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 0, A, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 9, A, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A + 2, A, 100, 2, A, A, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 2, A, A + 2, None, None, None) == F.FAIRY_ERR_INVALID_ARG
+    assert f(A, A, 100, 2, A, A, A + 1, None, None) == F.FAIRY_ERR_INVALID_ARG
