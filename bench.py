@@ -48,10 +48,11 @@ GEMV_KERNEL = "k_cgemv_lp<bf16,P=4,BCH=1> (one row per wave, lane-fixed planes)"
 # HBM bytes per launch of GEMV_KERNEL on this workload, from the FETCH_SIZE and
 # WRITE_SIZE counters scaled by a plain copy's (profiles/gemv_lp_bf16_2048x2048_S2_B1.md);
 # None whenever the kernel has changed since those counters were taken
-GEMV_TRAFFIC_BYTES = 4380672
-# SQ_ACTIVE_INST_VALU x 4 cycles / (1024 SIMDs x kernel cycles) of GEMV_KERNEL
-# from the same profile; None whenever the kernel has changed since
-GEMV_VALU_BUSY = None
+GEMV_TRAFFIC_BYTES = 4364288
+# SQ_ACTIVE_INST_VALU x 4 cycles / 1024 SIMDs over the kernel's traced
+# duration at the nominal 2.4 GHz, from the same profile; None whenever the
+# kernel has changed since
+GEMV_VALU_BUSY = 0.39
 POOL_BYTES = 512 << 20
 
 

@@ -403,14 +403,14 @@ __device__ __forceinline__ void lp_body(const GemvArgs& a, int blk)
     for (int i = 0; i < 2 * BCH; ++i)
         *((c0 < a.m64 && (i >> 1) < nb) ? x_dst(i >> 1, i & 1, c0) : spare) =
             make_uint4(xv[4 * i], xv[4 * i + 1], xv[4 * i + 2], xv[4 * i + 3]);
-    // rows longer than one pass of the block
+    // rows longer than one pass of the block: one piece at a time, the
+    // store unconditional like the first pass's (an array of pieces behind
+    // a per-column branch was kept in scratch memory)
     for (int c = c0 + kThreadsLp * per_elems; c < a.m64; c += kThreadsLp * per_elems) {
-        uint4 v[2 * BCH];
-#pragma unroll
-        for (int i = 0; i < 2 * BCH; ++i) v[i] = *x_src(i >> 1, i & 1, c);
 #pragma unroll
         for (int i = 0; i < 2 * BCH; ++i) {
-            if ((i >> 1) < nb) *x_dst(i >> 1, i & 1, c) = v[i];
+            const uint4 v = *x_src(i >> 1, i & 1, c);
+            *(((i >> 1) < nb) ? x_dst(i >> 1, i & 1, c) : spare) = v;
         }
     }
     // decoded weights are +-2: half-scales; W planes multiply conj(x)
