@@ -127,25 +127,35 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t count)
         p[i] = 0ull;
 }
 
-// Stage k: recompute R_k from W with the scales of stages < k (already on
-// the device), write code_k, and add |R_k| on the code's axis into the
-// stage's exponent buckets (block-local LDS buckets, flushed once per block).
-// Stage k: recompute R_k from W with the scales of stages < k (already on
-// the device), write code_k, and add |R_k| on the code's axis into the
-// stage's exponent buckets.  V = 4: each thread takes 4 consecutive elements
-// (float4 loads, one 32-bit store of 4 codes); V = 1 for unaligned arrays.
+// Stage K: recompute R_K from W with the scales of stages < K (already on
+// the device; K is a template parameter, so the residual steps are straight
+// code), write code_K, and add |R_K| on the code's axis into the stage's
+// exponent buckets.  V = 4: each thread takes 4 consecutive elements (float4
+// loads, one 32-bit store of 4 codes); V = 1 for unaligned arrays.
 // A block accumulates into kCopies interleaved LDS copies of the buckets,
 // then adds its nonzero buckets into global copy blockIdx % kGlobalCopies of
 // the stage's workspace (integer atomics: exact and order-independent; the
 // copies keep the blocks of a launch from contending on ~40 hot addresses).
+// The per-axis element counts are summed over the wave first and added by
+// one lane: a per-lane atomic on one LDS address is turned by the compiler
+// into a scalar loop over the wave's lanes, which cost more than the
+// element work.
 constexpr int kCopies = 2;
 constexpr int kGlobalCopies = 16;
 constexpr int kStageBlocks = 1024;
+constexpr int kMaxStages = 8;
 
-template <int V>
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+template <int V, int K>
 __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__ w_re,
                                                        const float* __restrict__ w_im, int64_t count,
-                                                       int32_t k, const float* __restrict__ scales,
+                                                       const float* __restrict__ scales,
                                                        uint8_t* __restrict__ codes,
                                                        unsigned long long* __restrict__ ws)
 {
@@ -155,72 +165,72 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
     __shared__ unsigned long long s_cnt[2];
     for (int t = threadIdx.x; t < kBuckets * kCopies; t += blockDim.x) s_buck[t] = 0ull;
     if (threadIdx.x < 2) s_cnt[threadIdx.x] = 0ull;
-    __syncthreads();
-
-    // the scales of the earlier stages, read once (uniform values; the
-    // residual loop below is unrolled, so none is indexed at run time)
-    float sre[8], sim[8];
+    // the scales of the earlier stages (uniform values)
+    float sre[K > 0 ? K : 1], sim[K > 0 ? K : 1];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        sre[j] = (j < k) ? scales[2 * j] : 0.0f;
-        sim[j] = (j < k) ? scales[2 * j + 1] : 0.0f;
+    for (int j = 0; j < K; ++j) {
+        sre[j] = scales[2 * j];
+        sim[j] = scales[2 * j + 1];
     }
+    __syncthreads();
     const int copy = threadIdx.x % kCopies;
     const int64_t nv = count / V;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const vec_t* vr = reinterpret_cast<const vec_t*>(w_re);
     const vec_t* vi = reinterpret_cast<const vec_t*>(w_im);
-    code_t* cout = reinterpret_cast<code_t*>(codes + (int64_t)k * count);
+    code_t* cout = reinterpret_cast<code_t*>(codes + (int64_t)K * count);
     uint32_t n_im = 0, n_all = 0;
-    // kUnroll grid-stride steps at a time: all their loads are issued before
-    // any of them is processed
+    // one element: K residual steps, then its code and its bucket
+    auto element = [&](float a, float b) -> uint32_t {
+#pragma unroll
+        for (int j = 0; j < K; ++j) residual_step(a, b, phase_code(a, b), sre[j], sim[j]);
+        const uint32_t c = phase_code(a, b);
+        const uint32_t axis = c & 1u;
+        n_im += axis;
+        const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
+        const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
+        const uint32_t sig = ex ? (man | 0x800000u) : man;
+        // unconditional (adding 0 for a zero magnitude changes nothing)
+        atomicAdd(&s_buck[(axis * 256u + (ex ? ex : 1u)) * kCopies + copy], (unsigned long long)sig);
+        return c;
+    };
+    auto vec = [&](const vec_t ra, const vec_t rb) -> code_t {
+        n_all += V;
+        if constexpr (V == 4) {
+            uint32_t p = element(ra.x, rb.x);
+            p |= element(ra.y, rb.y) << 8;
+            p |= element(ra.z, rb.z) << 16;
+            p |= element(ra.w, rb.w) << 24;
+            return p;
+        } else {
+            return (code_t)element(ra, rb);
+        }
+    };
+    // Whole tiles of kUnroll grid-stride steps: every thread has all of
+    // them, whose loads are issued before any is processed; then the rest
+    // one step at a time.
     constexpr int kUnroll = 4;
-    for (int64_t iv0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; iv0 < nv; iv0 += kUnroll * stride) {
+    const int64_t tile = kUnroll * stride;
+    const int64_t full = nv / tile;
+    int64_t iv0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t t = 0; t < full; ++t, iv0 += tile) {
         vec_t ra[kUnroll], rb[kUnroll];
 #pragma unroll
         for (int q = 0; q < kUnroll; ++q) {
-            const int64_t iv = iv0 + q * stride;
-            const int64_t il = iv < nv ? iv : iv0;  // a step past the end reloads the first (not processed)
-            ra[q] = vr[il];
-            rb[q] = vi[il];
+            ra[q] = vr[iv0 + q * stride];
+            rb[q] = vi[iv0 + q * stride];
         }
 #pragma unroll
-        for (int q = 0; q < kUnroll; ++q) {
-            const int64_t iv = iv0 + q * stride;
-            if (iv >= nv) break;
-            float av[V], bv[V];
-            if constexpr (V == 4) {
-                av[0] = ra[q].x; av[1] = ra[q].y; av[2] = ra[q].z; av[3] = ra[q].w;
-                bv[0] = rb[q].x; bv[1] = rb[q].y; bv[2] = rb[q].z; bv[3] = rb[q].w;
-            } else {
-                av[0] = ra[q];
-                bv[0] = rb[q];
-            }
-            uint32_t cpack = 0;
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                float a = av[e], b = bv[e];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (j < k) residual_step(a, b, phase_code(a, b), sre[j], sim[j]);
-                const uint32_t c = phase_code(a, b);
-                cpack |= c << (8 * e);
-                const uint32_t axis = c & 1u;
-                n_im += axis;
-                const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
-                const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
-                const uint32_t sig = ex ? (man | 0x800000u) : man;
-                // unconditional (adding 0 for a zero magnitude changes nothing)
-                atomicAdd(&s_buck[(axis * 256u + (ex ? ex : 1u)) * kCopies + copy], (unsigned long long)sig);
-            }
-            n_all += V;
-            cout[iv] = (code_t)cpack;
-        }
+        for (int q = 0; q < kUnroll; ++q) cout[iv0 + q * stride] = vec(ra[q], rb[q]);
     }
-    if (n_all - n_im) atomicAdd(&s_cnt[0], (unsigned long long)(n_all - n_im));
-    if (n_im) atomicAdd(&s_cnt[1], (unsigned long long)n_im);
+    for (int64_t iv = iv0; iv < nv; iv += stride) cout[iv] = vec(vr[iv], vi[iv]);
+    const uint32_t n_re_w = wave_sum_u32(n_all - n_im), n_im_w = wave_sum_u32(n_im);
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&s_cnt[0], (unsigned long long)n_re_w);
+        atomicAdd(&s_cnt[1], (unsigned long long)n_im_w);
+    }
     __syncthreads();
-    unsigned long long* g = ws + ((int64_t)k * kGlobalCopies + blockIdx.x % kGlobalCopies) * kStageWords;
+    unsigned long long* g = ws + ((int64_t)K * kGlobalCopies + blockIdx.x % kGlobalCopies) * kStageWords;
     for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) {
         unsigned long long v = 0ull;
 #pragma unroll
@@ -240,72 +250,20 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
 // when E > 0, so Q1 plus that sticky bit decide the rounding exactly.
 constexpr int kLimbs = 10;  // 320 bits
 
-constexpr int kFinThreads = 256;
+constexpr int kFinThreads = 256;  // one thread per exponent bucket of an axis
+constexpr int kFinParts = 16;     // first-round partial sums per limb
 
-__global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k,
-                                                              float* __restrict__ scales)
+// The exact mean of one axis rounded to fp32: limb q of N is lsum[q] (each
+// below 2^40, so the carries are taken here), cnt the number of entries.
+__device__ float exact_mean_f32(const unsigned long long (&lsum)[kLimbs], unsigned long long cnt)
 {
-    // 128 threads per axis; thread j splits buckets 2j and 2j+1 into 32-bit
-    // limb pieces, then a tree in LDS adds each limb over the 128 threads
-    // (fixed order, integer: exact)
-    __shared__ unsigned long long s_red[kFinThreads][kLimbs];
-    __shared__ unsigned long long s_part[2][kLimbs];
-    __shared__ unsigned long long s_b[kStageWords];
-    const int axis = threadIdx.x >> 7;
-    const int j = threadIdx.x & 127;
-    // buckets and counts: the sum of the stage's global copies
-    const unsigned long long* g0 = ws + (int64_t)k * kGlobalCopies * kStageWords;
-    for (int t = threadIdx.x; t < kStageWords; t += blockDim.x) {
-        unsigned long long v = 0ull;
-        for (int c = 0; c < kGlobalCopies; ++c) v += g0[(int64_t)c * kStageWords + t];
-        s_b[t] = v;
-    }
-    __syncthreads();
-    const unsigned long long* g = s_b;
-    unsigned long long part[kLimbs];
-#pragma unroll
-    for (int q = 0; q < kLimbs; ++q) part[q] = 0ull;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int eb = 2 * j + h;
-        const unsigned long long v = (eb >= 1) ? g[256 * axis + eb] : 0ull;
-        if (!v) continue;
-        // v * 2^(eb-1), seen limb by limb (limb q holds bits 32q .. 32q+31)
-#pragma unroll
-        for (int q = 0; q < kLimbs; ++q) {
-            const int sh = eb - 1 - 32 * q;
-            uint32_t piece;
-            if (sh >= 32 || sh <= -64) piece = 0u;
-            else if (sh >= 0) piece = (uint32_t)(v << sh);
-            else piece = (uint32_t)(v >> (-sh));
-            part[q] += piece;
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < kLimbs; ++q) s_red[threadIdx.x][q] = part[q];
-    __syncthreads();
-    for (int w = 64; w >= 1; w >>= 1) {
-        if (j < w) {
-#pragma unroll
-            for (int q = 0; q < kLimbs; ++q) s_red[threadIdx.x][q] += s_red[threadIdx.x + w][q];
-        }
-        __syncthreads();
-    }
-    if (j == 0) {
-#pragma unroll
-        for (int q = 0; q < kLimbs; ++q) s_part[axis][q] = s_red[threadIdx.x][q];
-    }
-    __syncthreads();
-    const int L = j;
-    if (L != 0) return;
-    const unsigned long long cnt = g[kBuckets + axis];
     float result = 0.0f;
     if (cnt != 0ull) {
         uint32_t N[kLimbs];
         unsigned long long carry = 0ull;
 #pragma unroll
         for (int q = 0; q < kLimbs; ++q) {
-            const unsigned long long t = s_part[axis][q] + carry;
+            const unsigned long long t = lsum[q] + carry;
             N[q] = (uint32_t)t;
             carry = t >> 32;
         }
@@ -359,7 +317,64 @@ __global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long
             result = __uint_as_float(bits);
         }
     }
-    scales[2 * k + axis] = result;
+    return result;
+}
+
+// Two blocks, one per axis.  Thread t owns exponent bucket t of the axis:
+// it adds the bucket's global copies (all loads at once), cuts
+// bucket * 2^(t-1) into 32-bit limb pieces, and the pieces of each limb are
+// added in two rounds through LDS (integer sums: exact in any order); one
+// thread then divides by the count and rounds.
+__global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k,
+                                                              float* __restrict__ scales)
+{
+    __shared__ unsigned long long s_piece[kLimbs][kFinThreads];
+    __shared__ unsigned long long s_part[kLimbs][kFinParts];
+    __shared__ unsigned long long s_cnt[kGlobalCopies];
+    const int axis = blockIdx.x;
+    const int eb = threadIdx.x;
+    const unsigned long long* g0 = ws + (int64_t)k * kGlobalCopies * kStageWords;
+    unsigned long long cv[kGlobalCopies];
+#pragma unroll
+    for (int c = 0; c < kGlobalCopies; ++c) cv[c] = g0[(int64_t)c * kStageWords + 256 * axis + eb];
+    // the copies of the axis's count, one per thread, in the same round of loads
+    if (eb < kGlobalCopies) s_cnt[eb] = g0[(int64_t)eb * kStageWords + kBuckets + axis];
+    unsigned long long v = 0ull;
+#pragma unroll
+    for (int c = 0; c < kGlobalCopies; ++c) v += cv[c];
+    if (eb == 0) v = 0ull;  // bucket 0 is never used (subnormals are in bucket 1)
+    // v * 2^(eb-1), seen limb by limb (limb q holds bits 32q .. 32q+31)
+#pragma unroll
+    for (int q = 0; q < kLimbs; ++q) {
+        const int sh = eb - 1 - 32 * q;
+        uint32_t piece;
+        if (sh >= 32 || sh <= -64) piece = 0u;
+        else if (sh >= 0) piece = (uint32_t)(v << sh);
+        else piece = (uint32_t)(v >> (-sh));
+        s_piece[q][eb] = piece;
+    }
+    __syncthreads();
+    if (threadIdx.x < kLimbs * kFinParts) {
+        const int q = threadIdx.x / kFinParts, part = threadIdx.x % kFinParts;
+        unsigned long long acc = 0ull;
+#pragma unroll
+        for (int i = 0; i < kFinThreads / kFinParts; ++i) acc += s_piece[q][part + kFinParts * i];
+        s_part[q][part] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    unsigned long long lsum[kLimbs];
+#pragma unroll
+    for (int q = 0; q < kLimbs; ++q) {
+        unsigned long long acc = 0ull;
+#pragma unroll
+        for (int part = 0; part < kFinParts; ++part) acc += s_part[q][part];
+        lsum[q] = acc;
+    }
+    unsigned long long cnt = 0ull;
+#pragma unroll
+    for (int c = 0; c < kGlobalCopies; ++c) cnt += s_cnt[c];
+    scales[2 * k + axis] = exact_mean_f32(lsum, cnt);
 }
 
 __global__ __launch_bounds__(kThreads) void k_pq_resid(const float* __restrict__ w_re,
@@ -505,6 +520,29 @@ hipError_t launch_real_to_complex(const float* R, int64_t n, int64_t m, float* u
     return hipGetLastError();
 }
 
+namespace {
+// stage k's kernel (k residual steps before its code)
+template <int V>
+hipError_t launch_stage(int32_t k, int grid, const float* w_re, const float* w_im, int64_t count, const float* scales,
+                        uint8_t* codes, unsigned long long* ws, hipStream_t s)
+{
+    const dim3 g(grid), b(kThreads);
+    switch (k) {
+    case 0: hipLaunchKernelGGL((k_pq_stage<V, 0>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    case 1: hipLaunchKernelGGL((k_pq_stage<V, 1>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    case 2: hipLaunchKernelGGL((k_pq_stage<V, 2>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    case 3: hipLaunchKernelGGL((k_pq_stage<V, 3>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    case 4: hipLaunchKernelGGL((k_pq_stage<V, 4>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    case 5: hipLaunchKernelGGL((k_pq_stage<V, 5>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    case 6: hipLaunchKernelGGL((k_pq_stage<V, 6>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    case 7: hipLaunchKernelGGL((k_pq_stage<V, 7>), g, b, 0, s, w_re, w_im, count, scales, codes, ws); break;
+    default: return hipErrorInvalidValue;
+    }
+    static_assert(kMaxStages == 8, "one case per stage");
+    return hipGetLastError();
+}
+}  // namespace
+
 size_t phasequant_workspace_bytes(int32_t stages)
 {
     return (size_t)stages * kGlobalCopies * kStageWords * sizeof(unsigned long long);
@@ -522,14 +560,10 @@ hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count
     const bool vec = count % 4 == 0 && ((((uintptr_t)w_re) | ((uintptr_t)w_im) | ((uintptr_t)codes)) % 16 == 0);
     const int grid = grid_for(vec ? count / 4 : count, kThreads, kStageBlocks);
     for (int32_t k = 0; k < stages; ++k) {
-        if (vec)
-            hipLaunchKernelGGL(k_pq_stage<4>, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, k,
-                               (const float*)scales, codes, ws);
-        else
-            hipLaunchKernelGGL(k_pq_stage<1>, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, k,
-                               (const float*)scales, codes, ws);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_pq_finalize, dim3(1), dim3(kFinThreads), 0, s, (const unsigned long long*)ws, k, scales);
+        if ((e = vec ? launch_stage<4>(k, grid, w_re, w_im, count, scales, codes, ws, s)
+                     : launch_stage<1>(k, grid, w_re, w_im, count, scales, codes, ws, s)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(k_pq_finalize, dim3(2), dim3(kFinThreads), 0, s, (const unsigned long long*)ws, k, scales);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (resid_re || resid_im) {
@@ -550,7 +584,7 @@ hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count
 // not a memset) before the first stage, so the array's previous contents do
 // not matter; calls that overlap on one GPU share the array and race.
 // ---------------------------------------------------------------------------
-constexpr size_t kPqScratchBytes = (size_t)8 * kGlobalCopies * kStageWords * sizeof(unsigned long long);
+constexpr size_t kPqScratchBytes = (size_t)kMaxStages * kGlobalCopies * kStageWords * sizeof(unsigned long long);
 static __device__ __align__(256) unsigned char scratch[kPqScratchBytes];
 
 constexpr int kMaxDevices = 64;
