@@ -734,9 +734,14 @@ def main():
         import oracle
         Rh = synth.real_layer(4096, 4096, 200)
         ur, ui, wr, wi = oracle.real_to_complex(Rh, n, m, f32=True)
+        t_q = time.perf_counter()
         cu, su, _, _ = oracle.phasequant(ur, ui, S, want_resid=False)
+        t_q = time.perf_counter() - t_q
         cw, sw, _, _ = oracle.phasequant(wr, wi, S, want_resid=False)
         oc = np.concatenate([cu, cw]); osc = np.concatenate([su, sw])
+        t_p = time.perf_counter()
+        oracle.pack(oc, F.FAIRY_LAYOUT_TILED64)
+        t_p = time.perf_counter() - t_p
         xr, xi = synth.bf16_to_f32(rb), synth.bf16_to_f32(ib)
 
         def oracle_rate(threads, seconds):
@@ -754,6 +759,12 @@ def main():
         all_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
         cores, reps, el = oracle_rate(all_threads, args.cpu_seconds)
         _, reps1, el1 = oracle_rate(1, args.cpu_seconds / 2)
+        # a 64-token slice of the M = 2048 prefill on the same layer (all threads)
+        oracle.set_threads(all_threads)
+        gx_r, gx_i = synth.bf16_gaussian((64, m), seed=204)
+        t_g = time.perf_counter()
+        oracle.cgemv_dense(oc, osc, S, True, synth.bf16_to_f32(gx_r), synth.bf16_to_f32(gx_i))
+        t_g = time.perf_counter() - t_g
         cpu_model = "unknown"
         try:
             with open("/proc/cpuinfo") as f:
@@ -772,6 +783,13 @@ def main():
                               "sample": f"{reps1} GEMVs on 1 thread, {el1:.1f}s"},
             "cpu_model": cpu_model, "nproc": os.cpu_count(),
             "affinity_cpus": len(os.sched_getaffinity(0)),
+            # the other steps of the path, each run once by the oracle on this host
+            "other_steps": {
+                "phasequant_S2_2048x2048_ms_1thread": round(t_q * 1e3, 2),
+                "pack_P4_2048x2048_tiled64_ms_1thread": round(t_p * 1e3, 2),
+                "prefill_2048x2048_S2_ms_per_token": round(t_g * 1e3 / 64, 3),
+                "prefill_sample": f"64 tokens of the M=2048 prefill, bf16 N(0,1), {all_threads} threads",
+            },
         }
 
     print(json.dumps(result), flush=True)
