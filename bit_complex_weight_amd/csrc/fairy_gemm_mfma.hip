@@ -74,8 +74,8 @@ struct Tiles {
     static constexpr int tok = 16 * TT;                     // tokens per block
     static constexpr int buf_bytes = 2 * tok * kRowBytes;   // re and im: 8 KiB per token tile
     static constexpr int dma_insts = buf_bytes / (64 * 16); // wave-instructions per chunk
-    // cross-wave sums: up to kWaves/2 writers x one component of a wave's tile
-    static constexpr int red_bytes = (kWaves / 2) * TT * kRT * 64 * 16;
+    // cross-wave sums: one component of every wave's partial tiles
+    static constexpr int red_bytes = kWaves * TT * kRT * 64 * 16;
     static_assert(dma_insts % kWaves == 0, "staging split");
     static_assert(2 * buf_bytes >= red_bytes, "cross-wave sums reuse the chunk buffers");
 };
@@ -241,9 +241,13 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
                                             int accumulate, float* part)
 {
     // This plane's contribution.  U planes: y_re += s_re A1 - s_im A2,
-    // y_im += s_re A3 + s_im A4; W planes multiply conj(x): A2 and A3 flip.
-    const float s_re = a.scales[2 * p], s_im = a.scales[2 * p + 1];
+    // y_im += s_re A3 + s_im A4; W planes multiply conj(x): A2 and A3 flip,
+    // the sign folded into the scale it multiplies.  The bf16 sums come from
+    // +-2 weights: half-scales (exact).
+    constexpr float kHalf = std::is_same<Acc, floatx4_t>::value ? 0.5f : 1.0f;
     const float sg = (p < a.S) ? 1.0f : -1.0f;
+    const float c_re = kHalf * a.scales[2 * p], c_im = kHalf * a.scales[2 * p + 1];
+    const float c_re_sg = sg * c_re, c_im_sg = sg * c_im;
     floatx4_t pr[TT][kRT], pi[TT][kRT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
@@ -254,11 +258,10 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
             for (int v = 0; v < 4; ++v) {
                 float f1, f2, f3, f4;
                 if constexpr (std::is_same<Acc, floatx4_t>::value) {
-                    // decoded weights are +-2: half-scales
-                    f1 = 0.5f * acc[0][tt][rt][v];
-                    f2 = 0.5f * acc[1][tt][rt][v];
-                    f3 = 0.5f * acc[2][tt][rt][v];
-                    f4 = 0.5f * acc[3][tt][rt][v];
+                    f1 = acc[0][tt][rt][v];
+                    f2 = acc[1][tt][rt][v];
+                    f3 = acc[2][tt][rt][v];
+                    f4 = acc[3][tt][rt][v];
                 } else {
                     const int t1 = acc[0][tt][rt][v], t2 = acc[1][tt][rt][v];
                     const int t3 = acc[2][tt][rt][v], t4 = acc[3][tt][rt][v];
@@ -274,45 +277,68 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
                     f3 = (float)t3;
                     f4 = (float)t4;
                 }
-                pr[tt][rt][v] = s_re * f1 - sg * (s_im * f2);
-                pi[tt][rt][v] = sg * (s_re * f3) + s_im * f4;
+                pr[tt][rt][v] = c_re * f1 - c_im_sg * f2;
+                pi[tt][rt][v] = c_re_sg * f3 + c_im * f4;
             }
         }
 
-    // Sum the Q planes of each row group: at each halving step the waves of
-    // the upper half write, the lower half adds (fixed order, no atomics).
+    // Sum the Q planes of each row group.  Token tile tt belongs to the wave
+    // of slot tt % Q: every wave writes its partial tiles of the others' to
+    // LDS, and each owner adds the Q partials of its tiles in a fixed order,
+    // (0 + 2) + (1 + 3), then stores them, so all waves share the stores.
+    // One component at a time: the two chunk buffers hold one.
+    floatx4_t fr[TT][kRT], fi[TT][kRT];  // this wave's finished tiles (those it owns)
     if constexpr (Q > 1) {
+        const int me = __builtin_amdgcn_readfirstlane(slot);
+        auto at = [&](int tt, int s, int rt) {
+            return red + ((((size_t)rg * TT + tt) * Q + s) * kRT + rt) * 64 + lane;
+        };
 #pragma unroll
-        for (int step = Q / 2; step >= 1; step /= 2) {
+        for (int comp = 0; comp < 2; ++comp) {
+            const floatx4_t (&mine)[TT][kRT] = comp ? pi : pr;
+            floatx4_t (&fin)[TT][kRT] = comp ? fi : fr;
+            __syncthreads();  // the buffers are free: the chunks (or the last component) are read
 #pragma unroll
-            for (int comp = 0; comp < 2; ++comp) {
-                floatx4_t (&part)[TT][kRT] = comp ? pi : pr;
-                __syncthreads();
-                if (slot >= step && slot < 2 * step) {
-                    floatx4_t* dst = red + (size_t)(rg * step + slot - step) * TT * kRT * 64;
+            for (int tt = 0; tt < TT; ++tt) {
+                if (tt % Q == me) continue;
 #pragma unroll
-                    for (int tt = 0; tt < TT; ++tt)
+                for (int rt = 0; rt < kRT; ++rt) *at(tt, me, rt) = mine[tt][rt];
+            }
+            __syncthreads();
 #pragma unroll
-                        for (int rt = 0; rt < kRT; ++rt) dst[(tt * kRT + rt) * 64 + lane] = part[tt][rt];
-                }
-                __syncthreads();
-                if (slot < step) {
-                    const floatx4_t* src = red + (size_t)(rg * step + slot) * TT * kRT * 64;
+            for (int tt = 0; tt < TT; ++tt) {
+                if (tt % Q != me) continue;
 #pragma unroll
-                    for (int tt = 0; tt < TT; ++tt)
+                for (int rt = 0; rt < kRT; ++rt) {
+                    floatx4_t v[Q];
 #pragma unroll
-                        for (int rt = 0; rt < kRT; ++rt) part[tt][rt] += src[(tt * kRT + rt) * 64 + lane];
+                    for (int s = 0; s < Q; ++s) {
+                        if (s == me) v[s] = mine[tt][rt];
+                        else v[s] = *at(tt, s, rt);
+                    }
+                    if constexpr (Q == 4)
+                        fin[tt][rt] = (v[0] + v[2]) + (v[1] + v[3]);
+                    else
+                        fin[tt][rt] = v[0] + v[1];
                 }
             }
         }
+    } else {
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+            for (int rt = 0; rt < kRT; ++rt) {
+                fr[tt][rt] = pr[tt][rt];
+                fi[tt][rt] = pi[tt][rt];
+            }
     }
-    if (slot != 0) return;
     if (part) {
         // split K: this block's share of the sum, [split][re/im][M][n]
         const int64_t mn = (int64_t)a.B * a.n;
         float* pre = part + (int64_t)blockIdx.z * 2 * mn;
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
+        for (int tt = 0; tt < TT; ++tt) {
+            if (tt % Q != slot) continue;
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt) {
                 const int row = row0 + 16 * rt + r16;
@@ -320,15 +346,17 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
                 for (int v = 0; v < 4; ++v) {
                     const int tok = tok0 + 16 * tt + 4 * q + v;
                     if (row < a.n && tok < a.B) {
-                        pre[(int64_t)tok * a.n + row] = pr[tt][rt][v];
-                        pre[mn + (int64_t)tok * a.n + row] = pi[tt][rt][v];
+                        pre[(int64_t)tok * a.n + row] = fr[tt][rt][v];
+                        pre[mn + (int64_t)tok * a.n + row] = fi[tt][rt][v];
                     }
                 }
             }
+        }
         return;
     }
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    for (int tt = 0; tt < TT; ++tt) {
+        if (tt % Q != slot) continue;
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
             const int row = row0 + 16 * rt + r16;
@@ -338,14 +366,15 @@ __device__ __forceinline__ void finish_tile(const GemvArgs& a, floatx4_t* red, c
                 if (row < a.n && tok < a.B) {
                     float* yr = a.y_re + (int64_t)tok * a.ldy + row;
                     float* yi = a.y_im + (int64_t)tok * a.ldy + row;
-                    float fr = accumulate ? *yr + pr[tt][rt][v] : pr[tt][rt][v];
-                    float fi = accumulate ? *yi + pi[tt][rt][v] : pi[tt][rt][v];
-                    gemv::rope_apply(a, row, tok, fr, fi);  // set on the last pass only
-                    *yr = fr;
-                    *yi = fi;
+                    float vr = accumulate ? *yr + fr[tt][rt][v] : fr[tt][rt][v];
+                    float vi = accumulate ? *yi + fi[tt][rt][v] : fi[tt][rt][v];
+                    gemv::rope_apply(a, row, tok, vr, vi);  // set on the last pass only
+                    *yr = vr;
+                    *yi = vi;
                 }
             }
         }
+    }
 }
 
 template <int XT, int Q, int TT>
