@@ -754,8 +754,9 @@ def main():
                 if el >= seconds or reps >= 100000:
                     return used, reps, el
 
-        # all the host cores this process may use (the box gives one GPU's
-        # share of the host; OMP_NUM_THREADS states it), then one core
+        # all the host cores this process may use (a GPU's share of a shared
+        # host can be fewer than the CPU count; OMP_NUM_THREADS states it),
+        # then one core
         all_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
         cores, reps, el = oracle_rate(all_threads, args.cpu_seconds)
         _, reps1, el1 = oracle_rate(1, args.cpu_seconds / 2)

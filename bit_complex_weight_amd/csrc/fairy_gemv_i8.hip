@@ -61,7 +61,7 @@ __device__ __forceinline__ void unit_i8(const uint4 cw, int g, const uint8_t* xs
 }
 
 // 4 rows (waves) per block: against 8, 2048^2 S=2 at B = 1 took 4.19 us
-// instead of 4.35-4.41 (same-box A/B); the bf16/fp32 kernel measured the
+// instead of 4.35-4.41 (A/B on one machine); the bf16/fp32 kernel measured the
 // same either way and keeps 8
 constexpr int kThreadsLpI8 = 256;
 
