@@ -86,30 +86,39 @@ __global__ __launch_bounds__(kThreads) void k_real_to_complex1(const float* __re
 // Quadrant of arg(a + ib) by exact comparisons: floor(2 theta/pi + 1/2) mod 4;
 // on |a| == |b| the floor sends theta = 45, 135, -135, -45 degrees to
 // codes 1, 2, 3, 0; zero (either sign) -> 0.
-// Written with selects only: a branch per element would diverge inside the
-// wave and cost scalar exec-mask instructions around every comparison.
-__device__ __forceinline__ uint32_t phase_code(float a, float b)
+// Stated per axis: the code lies on the imaginary axis (odd code) when
+// |b| > |a|, or on a tie of non-zero parts with equal signs (a == b != 0:
+// 45 and -135 degrees); its sign (code >= 2) is that of the part on its
+// axis, compared with 0, so a zero element (real axis, +0 or -0) gets code 0.
+// Inputs are finite.  Written with comparisons and selects only: a branch
+// per element would diverge inside the wave.
+struct Phase {
+    bool im;   // code on the imaginary axis (code & 1)
+    bool neg;  // code >= 2
+    float v;   // the part on the code's axis (b if im, else a)
+};
+
+__device__ __forceinline__ Phase phase_of(float a, float b)
 {
-    const float A = fabsf(a), B = fabsf(b);
-    const uint32_t c_re = a > 0.0f ? 0u : 2u;                                 // |a| > |b|
-    const uint32_t c_im = b > 0.0f ? 1u : 3u;                                 // |b| > |a|
-    const uint32_t c_tie = a > 0.0f ? (b > 0.0f ? 1u : 0u) : (b > 0.0f ? 2u : 3u);
-    const uint32_t c_eq = (A == 0.0f) ? 0u : c_tie;
-    return (A > B) ? c_re : ((B > A) ? c_im : c_eq);
+    Phase ph;
+    // bitwise on the comparisons: no short-circuit, so no exec-mask branch
+    ph.im = (fabsf(b) > fabsf(a)) | ((a == b) & (a != 0.0f));
+    ph.v = ph.im ? b : a;
+    ph.neg = ph.v < 0.0f;
+    return ph;
 }
+
+__device__ __forceinline__ uint32_t phase_code(const Phase& ph) { return (uint32_t)ph.im | ((uint32_t)ph.neg << 1); }
 
 // R <- R - (s_re Re(i^c) + i s_im Im(i^c)), one fp32 operation on the code's
 // axis: codes 0 / 1 subtract the scale, codes 2 / 3 subtract its negation
 // (x - (-s) is the same IEEE operation as x + s).
-__device__ __forceinline__ void residual_step(float& a, float& b, uint32_t c, float s_re, float s_im)
+__device__ __forceinline__ void residual_step(float& a, float& b, const Phase& ph, float s_re, float s_im)
 {
-    const bool neg = (c & 2u) != 0u;
-    const float dr = neg ? -s_re : s_re;
-    const float di = neg ? -s_im : s_im;
-    const bool re_axis = (c & 1u) == 0u;
-    const float na = a - dr, nb = b - di;
-    a = re_axis ? na : a;
-    b = re_axis ? b : nb;
+    const float s = ph.im ? s_im : s_re;
+    const float nv = ph.v - (ph.neg ? -s : s);
+    a = ph.im ? a : nv;
+    b = ph.im ? nv : b;
 }
 
 // Workspace per stage: 2 axes x 256 exponent buckets (uint64) + 2 counts.
@@ -183,16 +192,18 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
     // one element: K residual steps, then its code and its bucket
     auto element = [&](float a, float b) -> uint32_t {
 #pragma unroll
-        for (int j = 0; j < K; ++j) residual_step(a, b, phase_code(a, b), sre[j], sim[j]);
-        const uint32_t c = phase_code(a, b);
-        const uint32_t axis = c & 1u;
-        n_im += axis;
-        const uint32_t bits = __float_as_uint(axis ? fabsf(b) : fabsf(a));
-        const uint32_t ex = bits >> 23, man = bits & 0x7FFFFFu;
-        const uint32_t sig = ex ? (man | 0x800000u) : man;
+        for (int j = 0; j < K; ++j) residual_step(a, b, phase_of(a, b), sre[j], sim[j]);
+        const Phase ph = phase_of(a, b);
+        n_im += ph.im;
+        // |part on the axis|: exponent field ex (at least 1: subnormals go to
+        // bucket 1) and the 24-bit integer significand (mag - ex<<23 + 2^23
+        // is man + 2^23 for a normal value and man for a subnormal one)
+        const uint32_t mag = __float_as_uint(ph.v) & 0x7FFFFFFFu;
+        const uint32_t mx = mag > 0x800000u ? mag : 0x800000u;
+        const uint32_t sig = mag - (mx & 0x7F800000u) + 0x800000u;
         // unconditional (adding 0 for a zero magnitude changes nothing)
-        atomicAdd(&s_buck[(axis * 256u + (ex ? ex : 1u)) * kCopies + copy], (unsigned long long)sig);
-        return c;
+        atomicAdd(&s_buck[((ph.im ? 256u : 0u) + (mx >> 23)) * kCopies + copy], (unsigned long long)sig);
+        return phase_code(ph);
     };
     auto vec = [&](const vec_t ra, const vec_t rb) -> code_t {
         n_all += V;
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void k_pq_resid(const float* __restrict__
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
          i += (int64_t)gridDim.x * blockDim.x) {
         float a = w_re[i], b = w_im[i];
-        for (int j = 0; j < stages; ++j) residual_step(a, b, phase_code(a, b), scales[2 * j], scales[2 * j + 1]);
+        for (int j = 0; j < stages; ++j) residual_step(a, b, phase_of(a, b), scales[2 * j], scales[2 * j + 1]);
         if (r_re) r_re[i] = a;
         if (r_im) r_im[i] = b;
     }
