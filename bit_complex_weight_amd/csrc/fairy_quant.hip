@@ -262,7 +262,8 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
 constexpr int kLimbs = 10;  // 320 bits
 
 constexpr int kFinThreads = 256;  // one thread per exponent bucket of an axis
-constexpr int kFinParts = 16;     // first-round partial sums per limb
+constexpr int kFinParts = 16;     // threads per limb (a power of two dividing 64)
+static_assert(64 % kFinParts == 0 && (kFinParts & (kFinParts - 1)) == 0, "a limb's threads share one wave");
 
 // The exact mean of one axis rounded to fp32: limb q of N is lsum[q] (each
 // below 2^40, so the carries are taken here), cnt the number of entries.
@@ -334,13 +335,14 @@ __device__ float exact_mean_f32(const unsigned long long (&lsum)[kLimbs], unsign
 // Two blocks, one per axis.  Thread t owns exponent bucket t of the axis:
 // it adds the bucket's global copies (all loads at once), cuts
 // bucket * 2^(t-1) into 32-bit limb pieces, and the pieces of each limb are
-// added in two rounds through LDS (integer sums: exact in any order); one
-// thread then divides by the count and rounds.
+// added by kFinParts threads from LDS, then across those threads' lanes
+// (integer sums: exact in any order); one thread then divides by the count
+// and rounds.
 __global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k,
                                                               float* __restrict__ scales)
 {
     __shared__ unsigned long long s_piece[kLimbs][kFinThreads];
-    __shared__ unsigned long long s_part[kLimbs][kFinParts];
+    __shared__ unsigned long long s_lsum[kLimbs];
     __shared__ unsigned long long s_cnt[kGlobalCopies];
     const int axis = blockIdx.x;
     const int eb = threadIdx.x;
@@ -365,23 +367,25 @@ __global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long
         s_piece[q][eb] = piece;
     }
     __syncthreads();
-    if (threadIdx.x < kLimbs * kFinParts) {
+    {
+        // thread t < kLimbs * kFinParts sums every kFinParts-th piece of limb
+        // t / kFinParts; the kFinParts threads of a limb are consecutive lanes
+        // of one wave and finish the sum with a butterfly
         const int q = threadIdx.x / kFinParts, part = threadIdx.x % kFinParts;
         unsigned long long acc = 0ull;
+        if (q < kLimbs) {
 #pragma unroll
-        for (int i = 0; i < kFinThreads / kFinParts; ++i) acc += s_piece[q][part + kFinParts * i];
-        s_part[q][part] = acc;
+            for (int i = 0; i < kFinThreads / kFinParts; ++i) acc += s_piece[q][part + kFinParts * i];
+        }
+#pragma unroll
+        for (int off = kFinParts / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+        if (q < kLimbs && part == 0) s_lsum[q] = acc;
     }
     __syncthreads();
     if (threadIdx.x != 0) return;
     unsigned long long lsum[kLimbs];
 #pragma unroll
-    for (int q = 0; q < kLimbs; ++q) {
-        unsigned long long acc = 0ull;
-#pragma unroll
-        for (int part = 0; part < kFinParts; ++part) acc += s_part[q][part];
-        lsum[q] = acc;
-    }
+    for (int q = 0; q < kLimbs; ++q) lsum[q] = s_lsum[q];
     unsigned long long cnt = 0ull;
 #pragma unroll
     for (int c = 0; c < kGlobalCopies; ++c) cnt += s_cnt[c];
