@@ -450,11 +450,13 @@ __global__ __launch_bounds__(kThreads) void k_unpack_row16(const uint32_t* __res
     }
 }
 
-// TILED64, one thread per (row, 64-column group): for every plane it reads
-// the group's 64 codes (64 contiguous bytes; consecutive threads take
-// consecutive groups of a row, so a wave reads contiguous kilobytes) and
-// writes that plane's 16-byte unit; the P units of (row, group) are
-// contiguous, so consecutive planes complete the same lines.
+// TILED64, one thread per (row, 64-column group, plane), planes fastest:
+// the thread reads the group's 64 codes of its plane (64 contiguous bytes,
+// four 16-byte loads issued together) and writes that plane's 16-byte unit,
+// so a wave's stores cover 1 KiB of the output in order and its loads 16
+// groups of each plane.  (One thread per group walking the planes one at a
+// time kept only 64 bytes per thread in flight.)  I is the index type:
+// 32-bit unless the unit count needs more.
 __device__ __forceinline__ uint32_t pack_word16(const uint4 v)
 {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -464,28 +466,34 @@ __device__ __forceinline__ uint32_t pack_word16(const uint4 v)
     return word;
 }
 
+template <typename I>
 __global__ __launch_bounds__(kThreads) void k_pack_tiled(const uint8_t* __restrict__ codes, int32_t planes,
                                                          int64_t rows, int64_t m, uint32_t* __restrict__ out)
 {
-    const int64_t G = (m + 63) / 64;
-    const int64_t units = rows * G;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < units;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / G, g = i - r * G;
-        const int64_t c0 = 64 * g;
-        const int nw = (m - c0) >= 64 ? 4 : (int)((m - c0) >> 4);  // valid 16-column words
-        for (int p = 0; p < planes; ++p) {
-            const uint4* src = reinterpret_cast<const uint4*>(codes + ((int64_t)p * rows + r) * m + c0);
-            uint4 v[4];
+    const I G = (I)((m + 63) / 64);
+    const I total = (I)rows * G * (I)planes;
+    const I pl = (I)planes;
+    for (I t = (I)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (I)gridDim.x * blockDim.x) {
+        const I i = t / pl;
+        const int p = (int)(t - i * pl);
+        const I r = i / G, g = i - r * G;
+        const int64_t c0 = 64 * (int64_t)g;
+        const uint4* src = reinterpret_cast<const uint4*>(codes + ((int64_t)p * rows + (int64_t)r) * m + c0);
+        uint4 v[4];
+        if (m - c0 >= 64) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = src[u];
+        } else {
+            const int nw = (int)((m - c0) >> 4);  // valid 16-column words (m % 16 == 0)
 #pragma unroll
             for (int u = 0; u < 4; ++u) v[u] = (u < nw) ? src[u] : make_uint4(0, 0, 0, 0);
-            uint4 o;
-            o.x = pack_word16(v[0]);
-            o.y = pack_word16(v[1]);
-            o.z = pack_word16(v[2]);
-            o.w = pack_word16(v[3]);
-            reinterpret_cast<uint4*>(out)[(i * planes + p)] = o;
         }
+        uint4 o;
+        o.x = pack_word16(v[0]);
+        o.y = pack_word16(v[1]);
+        o.z = pack_word16(v[2]);
+        o.w = pack_word16(v[3]);
+        reinterpret_cast<uint4*>(out)[t] = o;  // unit (r, g) of plane p: (i * planes + p) = t
     }
 }
 
@@ -636,9 +644,12 @@ hipError_t launch_pack(const uint8_t* codes, int32_t planes, int64_t rows, int64
                        uint32_t* packed, hipStream_t s)
 {
     if (layout == FAIRY_LAYOUT_TILED64) {
-        const int64_t units = rows * ((m + 63) / 64);
-        hipLaunchKernelGGL(k_pack_tiled, dim3(grid_for(units, kThreads, 16384)), dim3(kThreads), 0, s, codes, planes,
-                           rows, m, packed);
+        const int64_t total = rows * ((m + 63) / 64) * planes;
+        const dim3 grid(grid_for(total, kThreads, 65536)), block(kThreads);
+        if (total + (int64_t)65536 * kThreads < ((int64_t)1 << 32))
+            hipLaunchKernelGGL(k_pack_tiled<uint32_t>, grid, block, 0, s, codes, planes, rows, m, packed);
+        else
+            hipLaunchKernelGGL(k_pack_tiled<uint64_t>, grid, block, 0, s, codes, planes, rows, m, packed);
         return hipGetLastError();
     }
     const int64_t nw = packed_words(rows, m, planes, layout);
