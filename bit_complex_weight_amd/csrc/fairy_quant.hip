@@ -149,7 +149,10 @@ __global__ void k_fill_u64(unsigned long long* __restrict__ p, int64_t count)
 // one lane: a per-lane atomic on one LDS address is turned by the compiler
 // into a scalar loop over the wave's lanes, which cost more than the
 // element work.
-constexpr int kCopies = 2;
+// Lanes of a wave mostly hit the same ~10 exponent buckets, and 64-bit LDS
+// atomics on one address are served one at a time: 8 interleaved copies
+// (32 KiB per block) cut those collisions; 2 copies measured ~7% slower.
+constexpr int kCopies = 8;
 constexpr int kGlobalCopies = 16;
 constexpr int kStageBlocks = 1024;
 constexpr int kMaxStages = 8;
