@@ -500,28 +500,31 @@ __global__ __launch_bounds__(kThreads) void k_pack_tiled(const uint8_t* __restri
     }
 }
 
+// The inverse, with the same thread mapping: one 16-byte unit in, the
+// group's 64 codes of that plane out.
+template <typename I>
 __global__ __launch_bounds__(kThreads) void k_unpack_tiled(const uint32_t* __restrict__ in, int32_t planes,
                                                            int64_t rows, int64_t m, uint8_t* __restrict__ codes)
 {
-    const int64_t G = (m + 63) / 64;
-    const int64_t units = rows * G;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < units;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / G, g = i - r * G;
-        const int64_t c0 = 64 * g;
+    const I G = (I)((m + 63) / 64);
+    const I total = (I)rows * G * (I)planes;
+    const I pl = (I)planes;
+    for (I t = (I)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (I)gridDim.x * blockDim.x) {
+        const I i = t / pl;
+        const int p = (int)(t - i * pl);
+        const I r = i / G, g = i - r * G;
+        const int64_t c0 = 64 * (int64_t)g;
         const int nw = (m - c0) >= 64 ? 4 : (int)((m - c0) >> 4);
-        for (int p = 0; p < planes; ++p) {
-            const uint4 wv = reinterpret_cast<const uint4*>(in)[i * planes + p];
-            const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
-            uint4* dst = reinterpret_cast<uint4*>(codes + ((int64_t)p * rows + r) * m + c0);
+        const uint4 wv = reinterpret_cast<const uint4*>(in)[t];
+        const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint4* dst = reinterpret_cast<uint4*>(codes + ((int64_t)p * rows + (int64_t)r) * m + c0);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (u >= nw) break;
-                uint32_t o[4] = {0u, 0u, 0u, 0u};
+        for (int u = 0; u < 4; ++u) {
+            if (u >= nw) break;
+            uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int t = 0; t < 16; ++t) o[t >> 2] |= ((words[u] >> tiled_bit(t)) & 3u) << (8 * (t & 3));
-                dst[u] = make_uint4(o[0], o[1], o[2], o[3]);
-            }
+            for (int k = 0; k < 16; ++k) o[k >> 2] |= ((words[u] >> tiled_bit(k)) & 3u) << (8 * (k & 3));
+            dst[u] = make_uint4(o[0], o[1], o[2], o[3]);
         }
     }
 }
@@ -664,9 +667,12 @@ hipError_t launch_unpack(const uint32_t* packed, int32_t planes, int64_t rows, i
                          uint8_t* codes, hipStream_t s)
 {
     if (layout == FAIRY_LAYOUT_TILED64) {
-        const int64_t units = rows * ((m + 63) / 64);
-        hipLaunchKernelGGL(k_unpack_tiled, dim3(grid_for(units, kThreads, 16384)), dim3(kThreads), 0, s, packed,
-                           planes, rows, m, codes);
+        const int64_t total = rows * ((m + 63) / 64) * planes;
+        const dim3 grid(grid_for(total, kThreads, 65536)), block(kThreads);
+        if (total + (int64_t)65536 * kThreads < ((int64_t)1 << 32))
+            hipLaunchKernelGGL(k_unpack_tiled<uint32_t>, grid, block, 0, s, packed, planes, rows, m, codes);
+        else
+            hipLaunchKernelGGL(k_unpack_tiled<uint64_t>, grid, block, 0, s, packed, planes, rows, m, codes);
         return hipGetLastError();
     }
     const int64_t nw = packed_words(rows, m, planes, layout);

@@ -76,7 +76,8 @@ def test_phasequant_all_one_axis():
 
 
 @pytest.mark.parametrize("layout", [F.FAIRY_LAYOUT_ROW16, F.FAIRY_LAYOUT_TILED64])
-@pytest.mark.parametrize("planes,rows,m", [(1, 1, 16), (1, 256, 256), (4, 37, 80), (6, 5, 5504), (4, 2048, 2048)])
+@pytest.mark.parametrize("planes,rows,m", [(1, 1, 16), (1, 256, 256), (4, 37, 80), (3, 129, 2096), (6, 5, 5504),
+                                           (4, 2048, 2048)])
 def test_pack_unpack_bit_exact(layout, planes, rows, m):
     log(f"pack layout={layout} planes={planes} rows={rows} m={m}")
     c = synth.random_codes((planes, rows, m), 1000 + rows)
