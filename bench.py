@@ -499,8 +499,17 @@ def main():
         ms_q = bn.graph_ms(lambda i: F.fairy_phasequant(pl[0], pl[1], L["count"], S, cd[0], sc[0], None, None, ws,
                                                         wsb), args.steps)
         ms_p = bn.graph_ms(lambda i: F.fairy_pack(cd, P, n, m, F.FAIRY_LAYOUT_TILED64, L["packed"]), args.steps)
+        # the whole conversion of the real layer in one call, checked against the steps
+        q_packed, q_scales = torch.empty_like(L["packed"]), torch.empty_like(L["scales"])
+        wsq = F.fairy_quantize_workspace_bytes(n, m, S, 1)
+        wq = torch.empty(wsq, dtype=torch.uint8, device="cuda")
+        ms_r = bn.graph_ms(lambda i: F.fairy_quantize_real(L["R"], n, m, S, q_packed, q_scales, wq, wsq), args.steps)
+        if not (torch.equal(q_packed, L["packed"]) and torch.equal(q_scales, L["scales"])):
+            raise SystemExit("fairy_quantize_real differs from the step-by-step conversion")
         print(json.dumps({"phasequant_S2_2048x2048": {"ms": ms_q, "unique_GB/s": (L["count"] * 8) / (ms_q * 1e-3) / 1e9},
-                          "pack_P4_2048x2048": {"ms": ms_p, "GB/s": (P * L["count"] * 1.25) / (ms_p * 1e-3) / 1e9}}),
+                          "pack_P4_2048x2048": {"ms": ms_p, "GB/s": (P * L["count"] * 1.25) / (ms_p * 1e-3) / 1e9},
+                          "quantize_real_4096x4096_S2": {"ms": ms_r,
+                                                         "R_GB/s": (4 * n * m * 4) / (ms_r * 1e-3) / 1e9}}),
               flush=True)
         return
     if args.layer:

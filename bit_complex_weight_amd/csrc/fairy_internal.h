@@ -125,6 +125,14 @@ hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count
                              uint8_t* codes, float* scales, float* resid_re, float* resid_im,
                              void* workspace, hipStream_t s);
 
+// PhaseQuant of both matrices of a real layer R [2n][2m], U and W formed
+// inside the stage kernels (no planes in memory): codes [2S][n*m] (U_1..U_S,
+// W_1..W_S), scales [2S][2] in the same order; bit-identical to the
+// conversion followed by launch_phasequant on U and on W.
+size_t phasequant_real_workspace_bytes(int32_t stages);
+hipError_t launch_phasequant_real(const float* R, int64_t n, int64_t m, int32_t stages, uint8_t* codes,
+                                  float* scales, void* workspace, hipStream_t s);
+
 // Device address (current device) and size of the static PhaseQuant bucket
 // array used by fairy_phasequant_noalloc.
 hipError_t phasequant_scratch(void** out);

@@ -25,10 +25,11 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace carve-up for a conversion: [4 fp32 planes (real input only)]
-// [codes P x n x m] [PhaseQuant buckets], each 256-byte aligned.
+// Workspace carve-up for a conversion: [codes P x n x m] [PhaseQuant
+// buckets: one matrix's for complex input, U's and W's for real input, whose
+// U and W are formed inside the PhaseQuant stages], each 256-byte aligned.
 struct Carve {
-    size_t planes, codes, pq, total;
+    size_t codes, pq, total;
 };
 
 bool carve(int64_t n, int64_t m, int32_t stages, int32_t has_conj, Carve* c)
@@ -38,10 +39,10 @@ bool carve(int64_t n, int64_t m, int32_t stages, int32_t has_conj, Carve* c)
     if (n * m >= ((int64_t)1 << 32)) return false;  // PhaseQuant element count
     const size_t count = (size_t)(n * m);
     const int32_t P = stages * (1 + has_conj);
-    c->planes = has_conj ? round_up(4 * count * sizeof(float), kAlign) : 0;
     c->codes = round_up((size_t)P * count, kAlign);
-    c->pq = round_up(fairy::phasequant_workspace_bytes(stages), kAlign);
-    c->total = c->planes + c->codes + c->pq;
+    c->pq = round_up(has_conj ? fairy::phasequant_real_workspace_bytes(stages) : fairy::phasequant_workspace_bytes(stages),
+                     kAlign);
+    c->total = c->codes + c->pq;
     return true;
 }
 
@@ -88,20 +89,13 @@ static fairy_status quantize(const float* R, const float* w_re, const float* w_i
     const hipStream_t s = as_stream(stream);
     const int64_t count = n * m;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    uint8_t* codes = ws + c.planes;
-    void* pq = ws + c.planes + c.codes;
+    uint8_t* codes = ws;
+    void* pq = ws + c.codes;
     (void)hipGetLastError();
     hipError_t e = hipSuccess;
     if (has_conj) {
-        float* planes = reinterpret_cast<float*>(ws);
-        float *ure = planes, *uim = planes + count, *wre = planes + 2 * count, *wim = planes + 3 * count;
-        if ((e = fairy::launch_real_to_complex(R, n, m, ure, uim, wre, wim, s)) != hipSuccess) return from_hip(e);
         // planes U_1..U_S, then W_1..W_S; scales follow the same order
-        if ((e = fairy::launch_phasequant(ure, uim, count, stages, codes, scales, nullptr, nullptr, pq, s)) !=
-            hipSuccess)
-            return from_hip(e);
-        if ((e = fairy::launch_phasequant(wre, wim, count, stages, codes + (size_t)stages * count, scales + 2 * stages,
-                                          nullptr, nullptr, pq, s)) != hipSuccess)
+        if ((e = fairy::launch_phasequant_real(R, n, m, stages, codes, scales, pq, s)) != hipSuccess)
             return from_hip(e);
     } else {
         if ((e = fairy::launch_phasequant(w_re, w_im, count, stages, codes, scales, nullptr, nullptr, pq, s)) !=

@@ -164,6 +164,50 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
     return v;
 }
 
+// One element of stage K: K residual steps with the earlier stages' scales,
+// then its code; |part on the code's axis| goes into its exponent bucket
+// (C interleaved LDS copies, this thread's copy `copy`): the exponent field
+// ex (at least 1: subnormals go to bucket 1) and the 24-bit integer
+// significand (mag - ex<<23 + 2^23 is man + 2^23 for a normal value and man
+// for a subnormal one).  The add is unconditional (adding 0 for a zero
+// magnitude changes nothing).
+template <int K, int C>
+__device__ __forceinline__ uint32_t pq_element(float a, float b, const float* sre, const float* sim,
+                                               unsigned long long* s_buck, int copy, uint32_t& n_im)
+{
+#pragma unroll
+    for (int j = 0; j < K; ++j) residual_step(a, b, phase_of(a, b), sre[j], sim[j]);
+    const Phase ph = phase_of(a, b);
+    n_im += ph.im;
+    const uint32_t mag = __float_as_uint(ph.v) & 0x7FFFFFFFu;
+    const uint32_t mx = mag > 0x800000u ? mag : 0x800000u;
+    const uint32_t sig = mag - (mx & 0x7F800000u) + 0x800000u;
+    atomicAdd(&s_buck[((ph.im ? 256u : 0u) + (mx >> 23)) * C + copy], (unsigned long long)sig);
+    return phase_code(ph);
+}
+
+// End of a block: the per-axis element counts (summed over each wave, added
+// by one lane into s_cnt), then the block's non-zero buckets into global
+// copy g of the stage's workspace.
+template <int C>
+__device__ __forceinline__ void pq_flush(const unsigned long long* s_buck, unsigned long long* s_cnt,
+                                         uint32_t n_re, uint32_t n_im, unsigned long long* g)
+{
+    const uint32_t n_re_w = wave_sum_u32(n_re), n_im_w = wave_sum_u32(n_im);
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&s_cnt[0], (unsigned long long)n_re_w);
+        atomicAdd(&s_cnt[1], (unsigned long long)n_im_w);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) {
+        unsigned long long v = 0ull;
+#pragma unroll
+        for (int c = 0; c < C; ++c) v += s_buck[t * C + c];
+        if (v) atomicAdd(&g[t], v);
+    }
+    if (threadIdx.x < 2 && s_cnt[threadIdx.x]) atomicAdd(&g[kBuckets + threadIdx.x], s_cnt[threadIdx.x]);
+}
+
 template <int V, int K>
 __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__ w_re,
                                                        const float* __restrict__ w_im, int64_t count,
@@ -192,21 +236,8 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
     const vec_t* vi = reinterpret_cast<const vec_t*>(w_im);
     code_t* cout = reinterpret_cast<code_t*>(codes + (int64_t)K * count);
     uint32_t n_im = 0, n_all = 0;
-    // one element: K residual steps, then its code and its bucket
     auto element = [&](float a, float b) -> uint32_t {
-#pragma unroll
-        for (int j = 0; j < K; ++j) residual_step(a, b, phase_of(a, b), sre[j], sim[j]);
-        const Phase ph = phase_of(a, b);
-        n_im += ph.im;
-        // |part on the axis|: exponent field ex (at least 1: subnormals go to
-        // bucket 1) and the 24-bit integer significand (mag - ex<<23 + 2^23
-        // is man + 2^23 for a normal value and man for a subnormal one)
-        const uint32_t mag = __float_as_uint(ph.v) & 0x7FFFFFFFu;
-        const uint32_t mx = mag > 0x800000u ? mag : 0x800000u;
-        const uint32_t sig = mag - (mx & 0x7F800000u) + 0x800000u;
-        // unconditional (adding 0 for a zero magnitude changes nothing)
-        atomicAdd(&s_buck[((ph.im ? 256u : 0u) + (mx >> 23)) * kCopies + copy], (unsigned long long)sig);
-        return phase_code(ph);
+        return pq_element<K, kCopies>(a, b, sre, sim, s_buck, copy, n_im);
     };
     auto vec = [&](const vec_t ra, const vec_t rb) -> code_t {
         n_all += V;
@@ -238,20 +269,88 @@ __global__ __launch_bounds__(kThreads) void k_pq_stage(const float* __restrict__
         for (int q = 0; q < kUnroll; ++q) cout[iv0 + q * stride] = vec(ra[q], rb[q]);
     }
     for (int64_t iv = iv0; iv < nv; iv += stride) cout[iv] = vec(vr[iv], vi[iv]);
-    const uint32_t n_re_w = wave_sum_u32(n_all - n_im), n_im_w = wave_sum_u32(n_im);
-    if ((threadIdx.x & 63) == 0) {
-        atomicAdd(&s_cnt[0], (unsigned long long)n_re_w);
-        atomicAdd(&s_cnt[1], (unsigned long long)n_im_w);
+    pq_flush<kCopies>(s_buck, s_cnt, n_all - n_im, n_im,
+                      ws + ((int64_t)K * kGlobalCopies + blockIdx.x % kGlobalCopies) * kStageWords);
+}
+
+// Stage K for both matrices of a real layer, read straight from R [2n][2m]:
+// U = ((R11 + R22) + i (R21 - R12)) / 2 and W = ((R11 - R22) + i (R12 + R21)) / 2
+// are formed per element by the conversion's own half_sum / half_diff, then
+// each goes through pq_element with its own scales and buckets.  Codes and
+// bucket sums therefore equal those of the conversion followed by the stage
+// kernel on U and on W, and the U, W planes are never written.  V = 4: four
+// consecutive columns (16-byte aligned R); a block holds both matrices'
+// buckets in LDS, four copies each.
+constexpr int kCopiesR = 4;
+
+template <int V, int K>
+__global__ __launch_bounds__(kThreads) void k_pq_real_stage(const float* __restrict__ R, int64_t n, int64_t m,
+                                                            const float* __restrict__ sc_u,
+                                                            const float* __restrict__ sc_w,
+                                                            uint8_t* __restrict__ codes_u,
+                                                            uint8_t* __restrict__ codes_w,
+                                                            unsigned long long* __restrict__ ws_u,
+                                                            unsigned long long* __restrict__ ws_w)
+{
+    typedef typename std::conditional<V == 4, float4, float>::type vec_t;
+    typedef typename std::conditional<V == 4, uint32_t, uint8_t>::type code_t;
+    __shared__ unsigned long long s_buck[2][kBuckets * kCopiesR];
+    __shared__ unsigned long long s_cnt[2][2];
+    for (int t = threadIdx.x; t < 2 * kBuckets * kCopiesR; t += blockDim.x) (&s_buck[0][0])[t] = 0ull;
+    if (threadIdx.x < 4) (&s_cnt[0][0])[threadIdx.x] = 0ull;
+    float sre_u[K > 0 ? K : 1], sim_u[K > 0 ? K : 1], sre_w[K > 0 ? K : 1], sim_w[K > 0 ? K : 1];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        sre_u[j] = sc_u[2 * j];
+        sim_u[j] = sc_u[2 * j + 1];
+        sre_w[j] = sc_w[2 * j];
+        sim_w[j] = sc_w[2 * j + 1];
     }
     __syncthreads();
-    unsigned long long* g = ws + ((int64_t)K * kGlobalCopies + blockIdx.x % kGlobalCopies) * kStageWords;
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) {
-        unsigned long long v = 0ull;
-#pragma unroll
-        for (int c = 0; c < kCopies; ++c) v += s_buck[t * kCopies + c];
-        if (v) atomicAdd(&g[t], v);
-    }
-    if (threadIdx.x < 2 && s_cnt[threadIdx.x]) atomicAdd(&g[kBuckets + threadIdx.x], s_cnt[threadIdx.x]);
+    const int copy = threadIdx.x % kCopiesR;
+    const int64_t count = n * m;
+    const uint32_t mv = (uint32_t)(m / V);       // vectors per row of U / W
+    const uint32_t nv = (uint32_t)(count / V);   // count < 2^32
+    const int64_t ldv = 2 * (int64_t)mv;         // vectors per row of R
+    const vec_t* Rv = reinterpret_cast<const vec_t*>(R);
+    code_t* cu = reinterpret_cast<code_t*>(codes_u + (int64_t)K * count);
+    code_t* cw = reinterpret_cast<code_t*>(codes_w + (int64_t)K * count);
+    uint32_t n_im_u = 0, n_im_w = 0, n_all = 0;
+    auto one = [&](float r11, float r12, float r21, float r22, uint32_t& cu1, uint32_t& cw1) {
+        cu1 = pq_element<K, kCopiesR>(half_sum(r11, r22), half_diff(r21, r12), sre_u, sim_u, s_buck[0], copy,
+                                      n_im_u);
+        cw1 = pq_element<K, kCopiesR>(half_diff(r11, r22), half_sum(r12, r21), sre_w, sim_w, s_buck[1], copy,
+                                      n_im_w);
+    };
+    // vector iv of U / W: row i = iv / mv, vector column j; its R vectors
+    // are R11 = (i, j), R12 = (i, mv + j), R21 = (n + i, j), R22 = (n + i, mv + j)
+    auto vec = [&](uint32_t iv) {
+        const uint32_t i = iv / mv, j = iv - i * mv;
+        const int64_t top = (int64_t)i * ldv + j, bot = ((int64_t)n + i) * ldv + j;
+        const vec_t r11 = Rv[top], r12 = Rv[top + mv], r21 = Rv[bot], r22 = Rv[bot + mv];
+        n_all += V;
+        if constexpr (V == 4) {
+            uint32_t pu = 0u, pw = 0u, a, b;
+            one(r11.x, r12.x, r21.x, r22.x, a, b); pu |= a;       pw |= b;
+            one(r11.y, r12.y, r21.y, r22.y, a, b); pu |= a << 8;  pw |= b << 8;
+            one(r11.z, r12.z, r21.z, r22.z, a, b); pu |= a << 16; pw |= b << 16;
+            one(r11.w, r12.w, r21.w, r22.w, a, b); pu |= a << 24; pw |= b << 24;
+            cu[iv] = pu;
+            cw[iv] = pw;
+        } else {
+            uint32_t a, b;
+            one(r11, r12, r21, r22, a, b);
+            cu[iv] = (code_t)a;
+            cw[iv] = (code_t)b;
+        }
+    };
+    // 64-bit loop index (nv + stride may pass 2^32); iv < nv < 2^32 inside
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t iv = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; iv < (int64_t)nv; iv += stride)
+        vec((uint32_t)iv);
+    const int64_t gcopy = ((int64_t)K * kGlobalCopies + blockIdx.x % kGlobalCopies) * kStageWords;
+    pq_flush<kCopiesR>(s_buck[0], s_cnt[0], n_all - n_im_u, n_im_u, ws_u + gcopy);
+    pq_flush<kCopiesR>(s_buck[1], s_cnt[1], n_all - n_im_w, n_im_w, ws_w + gcopy);
 }
 
 // Exact mean -> fp32, nearest even.
@@ -335,15 +434,20 @@ __device__ float exact_mean_f32(const unsigned long long (&lsum)[kLimbs], unsign
     return result;
 }
 
-// Two blocks, one per axis.  Thread t owns exponent bucket t of the axis:
+// Two blocks per matrix, one per axis.  Thread t owns exponent bucket t of the axis:
 // it adds the bucket's global copies (all loads at once), cuts
 // bucket * 2^(t-1) into 32-bit limb pieces, and the pieces of each limb are
 // added by kFinParts threads from LDS, then across those threads' lanes
 // (integer sums: exact in any order); one thread then divides by the count
 // and rounds.
-__global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long long* __restrict__ ws, int32_t k,
-                                                              float* __restrict__ scales)
+__global__ __launch_bounds__(kFinThreads) void k_pq_finalize(const unsigned long long* __restrict__ ws_a, int32_t k,
+                                                              float* __restrict__ scales_a,
+                                                              const unsigned long long* __restrict__ ws_b,
+                                                              float* __restrict__ scales_b)
 {
+    // blockIdx.y picks the matrix (a second one only for a real layer's U, W)
+    const unsigned long long* ws = blockIdx.y ? ws_b : ws_a;
+    float* scales = blockIdx.y ? scales_b : scales_a;
     __shared__ unsigned long long s_piece[kLimbs][kFinThreads];
     __shared__ unsigned long long s_lsum[kLimbs];
     __shared__ unsigned long long s_cnt[kGlobalCopies];
@@ -592,12 +696,72 @@ hipError_t launch_phasequant(const float* w_re, const float* w_im, int64_t count
         if ((e = vec ? launch_stage<4>(k, grid, w_re, w_im, count, scales, codes, ws, s)
                      : launch_stage<1>(k, grid, w_re, w_im, count, scales, codes, ws, s)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(k_pq_finalize, dim3(2), dim3(kFinThreads), 0, s, (const unsigned long long*)ws, k, scales);
+        hipLaunchKernelGGL(k_pq_finalize, dim3(2, 1), dim3(kFinThreads), 0, s, (const unsigned long long*)ws, k, scales,
+                           (const unsigned long long*)nullptr, (float*)nullptr);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (resid_re || resid_im) {
         hipLaunchKernelGGL(k_pq_resid, dim3(grid), dim3(kThreads), 0, s, w_re, w_im, count, stages,
                            (const float*)scales, resid_re, resid_im);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+namespace {
+template <int V>
+hipError_t launch_real_stage(int32_t k, int grid, const float* R, int64_t n, int64_t m, const float* sc_u,
+                             const float* sc_w, uint8_t* codes_u, uint8_t* codes_w, unsigned long long* ws_u,
+                             unsigned long long* ws_w, hipStream_t s)
+{
+    const dim3 g(grid), b(kThreads);
+    switch (k) {
+#define FAIRY_REAL_STAGE(K)                                                                                      \
+    case K:                                                                                                      \
+        hipLaunchKernelGGL((k_pq_real_stage<V, K>), g, b, 0, s, R, n, m, sc_u, sc_w, codes_u, codes_w, ws_u, ws_w); \
+        break;
+        FAIRY_REAL_STAGE(0)
+        FAIRY_REAL_STAGE(1)
+        FAIRY_REAL_STAGE(2)
+        FAIRY_REAL_STAGE(3)
+        FAIRY_REAL_STAGE(4)
+        FAIRY_REAL_STAGE(5)
+        FAIRY_REAL_STAGE(6)
+        FAIRY_REAL_STAGE(7)
+#undef FAIRY_REAL_STAGE
+    default: return hipErrorInvalidValue;
+    }
+    static_assert(kMaxStages == 8, "one case per stage");
+    return hipGetLastError();
+}
+}  // namespace
+
+size_t phasequant_real_workspace_bytes(int32_t stages) { return 2 * phasequant_workspace_bytes(stages); }
+
+hipError_t launch_phasequant_real(const float* R, int64_t n, int64_t m, int32_t stages, uint8_t* codes,
+                                  float* scales, void* workspace, hipStream_t s)
+{
+    const int64_t count = n * m;
+    const int64_t per = (int64_t)stages * kGlobalCopies * kStageWords;  // one matrix's words
+    unsigned long long* ws_u = (unsigned long long*)workspace;
+    unsigned long long* ws_w = ws_u + per;
+    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(2 * per, kThreads, 256)), dim3(kThreads), 0, s, ws_u, 2 * per);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // U planes 0..S-1 and scales [0, 2S); W planes S..2S-1 and scales [2S, 4S)
+    uint8_t* codes_u = codes;
+    uint8_t* codes_w = codes + (int64_t)stages * count;
+    float* sc_u = scales;
+    float* sc_w = scales + 2 * stages;
+    const bool vec = m % 4 == 0 && ((uintptr_t)R % 16 == 0) && ((uintptr_t)codes % 4 == 0) && count % 4 == 0;
+    const int grid = grid_for(vec ? count / 4 : count, kThreads, kStageBlocks);
+    for (int32_t k = 0; k < stages; ++k) {
+        if ((e = vec ? launch_real_stage<4>(k, grid, R, n, m, sc_u, sc_w, codes_u, codes_w, ws_u, ws_w, s)
+                     : launch_real_stage<1>(k, grid, R, n, m, sc_u, sc_w, codes_u, codes_w, ws_u, ws_w, s)) !=
+            hipSuccess)
+            return e;
+        hipLaunchKernelGGL(k_pq_finalize, dim3(2, 2), dim3(kFinThreads), 0, s, (const unsigned long long*)ws_u, k,
+                           sc_u, (const unsigned long long*)ws_w, sc_w);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

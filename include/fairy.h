@@ -305,6 +305,9 @@ fairy_status fairy_cgemm_rope(const fairy_clinear* L, const void* x_re, const vo
  * [Fairy2i article §2.1 (widely-linear split), §3.1-§3.2 (PhaseQuant codes and
  * axis scales), §4.1 (recursive residual stages)]: the steps above chained on
  * `stream` with every intermediate in `workspace`, ending in TILED64 words.
+ * For a real layer the PhaseQuant stages read R and form U and W themselves
+ * (the same rounding as fairy_real_to_complex), so the U, W planes never
+ * reach memory; the workspace holds the byte codes and the buckets.
  *
  * Workspace bytes for a conversion (0 for invalid arguments): has_conj = 1
  * for fairy_quantize_real, 0 for fairy_quantize_complex. */

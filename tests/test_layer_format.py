@@ -77,10 +77,11 @@ def test_read_info_truncated():
 
 
 def test_quantize_workspace_bytes():
-    # real: 4 fp32 planes + 2S code planes + S x 16 copies of 514 uint64, each 256-aligned
+    # real: 2S code planes + U's and W's buckets (S x 16 copies of 514 uint64
+    # each), each region 256-aligned; U and W are formed inside PhaseQuant
     n, m, S = 2048, 2048, 2
     pq = S * 16 * 514 * 8
-    want = 4 * n * m * 4 + 2 * S * n * m + ((pq + 255) // 256) * 256
+    want = 2 * S * n * m + ((2 * pq + 255) // 256) * 256
     assert F.fairy_quantize_workspace_bytes(n, m, S, 1) == want
     assert F.fairy_quantize_workspace_bytes(n, m, S, 0) == S * n * m + ((pq + 255) // 256) * 256
     assert F.fairy_quantize_workspace_bytes(0, m, S, 1) == 0
