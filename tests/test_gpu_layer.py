@@ -47,6 +47,36 @@ def test_quantize_real_bit_exact(n, m, S, seed):
     assert np.array_equal(host(L.scales).view(np.uint32), scales.view(np.uint32))
 
 
+def test_quantize_real_edge_values():
+    """U and W are formed inside the PhaseQuant stages: the split's single
+    rounding must hold where an fp32 sum would not give it directly (zero and
+    cancelling sums, subnormal halves, halves at the bottom of the normal
+    range, sums that overflow fp32) and beside ordinary values in one vector."""
+    n, m, S = 64, 256, 2
+    R = synth.real_layer(2 * n, 2 * m, 7)
+    tiny = np.float32(np.ldexp(1.5, -126))      # R11 + 0 = 1.5 * 2^-126: its half is subnormal
+    sub = np.float32(np.ldexp(3.0, -149))       # subnormal input
+    low = np.float32(np.ldexp(1.0, -125))       # half exactly 2^-126, the smallest normal
+    big = np.float32(3.0e38)                    # big + big overflows fp32, its half does not
+    def put(i, j, r11, r12, r21, r22):
+        R[i, j], R[i, m + j], R[n + i, j], R[n + i, m + j] = r11, r12, r21, r22
+    put(0, 0, 0.0, 0.0, 0.0, 0.0)
+    put(0, 1, -0.0, 0.0, -0.0, 0.0)
+    put(0, 2, 0.5, 0.25, 0.25, -0.5)            # R11 + R22 = 0, R21 - R12 = 0
+    put(1, 4, tiny, 0.0, sub, 0.0)
+    put(1, 5, low, -low, low, 0.0)
+    put(2, 8, big, big, -big, big)              # Re U, Im W, Re W, Im U from +-big pairs
+    put(2, 9, -big, big, big, -big)
+    put(3, 12, big, -sub, tiny, -big)
+    put(5, 17, sub, sub, -sub, sub)
+    log(f"quantize_real edge values n={n} m={m} S={S}")
+    L = quantize_real_gpu(R, n, m, S)
+    torch().cuda.synchronize()
+    words, scales, _ = oracle_real(R, n, m, S)
+    assert np.array_equal(host(L.packed).view(np.uint32), words)
+    assert np.array_equal(host(L.scales).view(np.uint32), scales.view(np.uint32))
+
+
 @pytest.mark.parametrize("n,m,S,sigma,seed", [(130, 256, 2, 1.0, 3), (2048, 2048, 2, 0.02 / np.sqrt(2), 500)])
 def test_quantize_complex_bit_exact(n, m, S, sigma, seed):
     log(f"quantize_complex n={n} m={m} S={S}")
