@@ -77,6 +77,43 @@ def test_quantize_real_edge_values():
     assert np.array_equal(host(L.scales).view(np.uint32), scales.view(np.uint32))
 
 
+def test_quantize_real_unaligned_input():
+    """R 4-byte aligned but not 16: the stages read it one element at a time."""
+    n, m, S = 48, 160, 2
+    R = synth.real_layer(2 * n, 2 * m, 11)
+    t = torch()
+    buf = t.zeros(R.size + 4, dtype=t.float32, device="cuda")
+    view = buf[1:1 + R.size]
+    assert view.data_ptr() % 16 == 4
+    view.copy_(dev(R.reshape(-1)))
+    P = 2 * S
+    packed = t.empty(F.fairy_packed_words(n, m, P, F.FAIRY_LAYOUT_TILED64), dtype=t.int32, device="cuda")
+    scales = t.empty((P, 2), dtype=t.float32, device="cuda")
+    wsb = F.fairy_quantize_workspace_bytes(n, m, S, 1)
+    ws = t.empty(wsb, dtype=t.uint8, device="cuda")
+    log(f"quantize_real unaligned n={n} m={m} S={S}")
+    F.fairy_quantize_real(view, n, m, S, packed, scales, ws, wsb)
+    t.cuda.synchronize()
+    words, sc, _ = oracle_real(R, n, m, S)
+    assert np.array_equal(host(packed).view(np.uint32), words)
+    assert np.array_equal(host(scales).view(np.uint32), sc.view(np.uint32))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_quantize_real_random_shapes(case):
+    g = np.random.default_rng(900 + case)
+    n = int(g.integers(1, 200))
+    m = 16 * int(g.integers(1, 40))
+    S = int(g.integers(1, 4))
+    log(f"quantize_real random case={case} n={n} m={m} S={S}")
+    R = synth.real_layer(2 * n, 2 * m, 950 + case)
+    L = quantize_real_gpu(R, n, m, S)
+    torch().cuda.synchronize()
+    words, scales, _ = oracle_real(R, n, m, S)
+    assert np.array_equal(host(L.packed).view(np.uint32), words)
+    assert np.array_equal(host(L.scales).view(np.uint32), scales.view(np.uint32))
+
+
 @pytest.mark.parametrize("n,m,S,sigma,seed", [(130, 256, 2, 1.0, 3), (2048, 2048, 2, 0.02 / np.sqrt(2), 500)])
 def test_quantize_complex_bit_exact(n, m, S, sigma, seed):
     log(f"quantize_complex n={n} m={m} S={S}")
