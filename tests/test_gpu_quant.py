@@ -68,6 +68,17 @@ def test_phasequant_edge_values():
     _check_pq(re, im, 3)
 
 
+@pytest.mark.parametrize("count", [3000, 4097])
+def test_phasequant_all_zero(count):
+    """A zero matrix (both signs of zero): every code 0, s_re the mean of
+    zeros and s_im over an empty set, both 0, and the residuals keep each
+    zero's sign (x - 0 is x)."""
+    g = np.random.default_rng(count)
+    re = np.where(g.random(count) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    im = np.where(g.random(count) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    _check_pq(re, im, 3)
+
+
 def test_phasequant_all_one_axis():
     """Every code on the real axis: s_im's set is empty, so s_im = 0."""
     re = synth.gaussian(1000, 1.0, 3)
