@@ -59,6 +59,25 @@ def test_graph_phasequant_and_pack():
     replay_check(call, [codes, scales, rr, ri, packed], clobber)
 
 
+def test_graph_quantize_real():
+    """The one-call real-layer conversion (U and W formed inside the
+    PhaseQuant stages, two matrices per launch) under replay."""
+    t = torch()
+    n, m, S = 96, 320, 2
+    R = dev(synth.real_layer(2 * n, 2 * m, 65))
+    P = 2 * S
+    packed = t.empty(F.fairy_packed_words(n, m, P, F.FAIRY_LAYOUT_TILED64), dtype=t.int32, device="cuda")
+    scales = t.empty((P, 2), dtype=t.float32, device="cuda")
+    wsb = F.fairy_quantize_workspace_bytes(n, m, S, 1)
+    ws = t.empty(wsb, dtype=t.uint8, device="cuda")
+
+    def clobber():
+        for b in (packed, scales, ws):
+            b.fill_(7)
+    log("graph: quantize_real")
+    replay_check(lambda: F.fairy_quantize_real(R, n, m, S, packed, scales, ws, wsb), [packed, scales], clobber)
+
+
 @pytest.mark.parametrize("xdtype", [F.FAIRY_BF16, F.FAIRY_I8])
 def test_graph_gemv(xdtype):
     t = torch()
